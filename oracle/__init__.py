@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for causal attention -- test infrastructure only (see attn_ref.py)."""
+from .attn_ref import (  # noqa: F401
+    attention_backward,
+    attention_decode,
+    attention_forward,
+    rms_normalize,
+    rope_rotate,
+    rope_unrotate,
+    visible_mask,
+)

@@ -1,0 +1,283 @@
+"""Plain fp64 CPU oracle for causal self-attention: forward, backward and KV-cache decode.
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product: only the
+test-suite (``tests/``), the smoke check in ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code with the
+HIP library, and imports nothing from it.
+
+What it computes (sources, by page title and section):
+
+* The attention definition, softmax(Q K^T / sqrt(d_k)) V, applied per head, and the
+  causal rule that scores of future positions are set to -inf before the softmax --
+  "GPT pretraining" page (dekermanjian, llm_gpt_pretrain), section "Multihead
+  Attention" (the definition and the MultiHeadAttention listing).  The mask there is
+  "upper triangle above the diagonal is masked"; the MiniGPT page ("Build and Train
+  a MiniGPT with JAX", section "Model Architecture") states the same rule as
+  "lower triangle including the diagonal is allowed".
+* Heads laid out as [B, H, T, d] (the ``_split_heads`` reshape/transpose in the same
+  listing).
+* Grouped-query attention (8 query heads over 4 KV heads), RoPE, parameter-free
+  RMSNorm QK-norm ("no learnable scale") and logit soft-capping -- nanoGPT-JAX 181M
+  model card, section "Architecture" (table and "Design choices worth naming");
+  the same features and the sliding window are named on the flaxchat page, section
+  "Core Features".
+* KV-cache decode: one new query attends over every cached key; with
+  offset = k_len - q_len, query i may see key j iff j <= offset + i -- "GPT
+  pretraining" page, section "Bonus: KV Caching".
+
+Readings of what the pages leave open (each also listed with its reason in the
+project's design notes):
+
+* RoPE pairs element i with element i + d/2 (half split), rotates by +p*w_i with
+  w_i = base^(-2i/d), and is applied to the whole head dimension.
+* RMSNorm: x / sqrt(mean(x^2) + eps), eps passed in (default 1e-6), applied to the
+  RoPE-rotated row (the two commute: RoPE is a rotation and keeps mean(x^2)).
+* The soft-cap acts on the scaled scores before the mask: s <- c * tanh(s / c).
+* Query head h reads KV head floor(h / (Hq / Hkv)) (contiguous groups).
+* Sliding window W > 0: key j is visible to query i iff i - W < j <= i.
+* Decode: the cache already holds the new token's (rotated) key/value, so the query
+  sits at position L_b - 1 and sees all L_b cached keys; a sequence with L_b = 0
+  yields an all-zero output row.
+
+Everything is computed densely per (batch, head) in float64 with numpy; there is
+no tiling, fusion or reordering beyond the definitions above.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_rotate",
+    "rope_unrotate",
+    "rms_normalize",
+    "visible_mask",
+    "attention_forward",
+    "attention_backward",
+    "attention_decode",
+]
+
+
+# --------------------------------------------------------------------------------------
+# Q/K prologue pieces (nanoGPT-JAX 181M model card, "Architecture": RoPE, QK-norm)
+# --------------------------------------------------------------------------------------
+def _rope_angles(positions: np.ndarray, d: int, base: float) -> np.ndarray:
+    """Angles a[t, i] = p_t * base^(-2i/d) for i < d/2 (float64, shape [len(positions), d/2])."""
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    omega = np.power(float(base), -2.0 * i / d)
+    return np.asarray(positions, dtype=np.float64)[:, None] * omega[None, :]
+
+
+def rope_rotate(x: np.ndarray, positions: np.ndarray, base: float = 10000.0) -> np.ndarray:
+    """Rotate each pair (x_i, x_{i+d/2}) of the rows of x[..., T, d] by the angle p_t * w_i.
+
+    (x_i, x_{i+d/2}) -> (x_i cos a - x_{i+d/2} sin a,  x_i sin a + x_{i+d/2} cos a).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    a = _rope_angles(positions, d, base)
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def rope_unrotate(y: np.ndarray, positions: np.ndarray, base: float = 10000.0) -> np.ndarray:
+    """The transpose (= inverse) of :func:`rope_rotate`: rotate every pair by -p_t * w_i.
+
+    Because the rotation is orthogonal, this is also the map that carries a gradient
+    with respect to the rotated row back to the raw row.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    d = y.shape[-1]
+    a = _rope_angles(positions, d, base)
+    c, s = np.cos(a), np.sin(a)
+    y1, y2 = y[..., : d // 2], y[..., d // 2:]
+    return np.concatenate([y1 * c + y2 * s, -y1 * s + y2 * c], axis=-1)
+
+
+def rms_normalize(x: np.ndarray, eps: float = 1e-6):
+    """Parameter-free RMSNorm of every row: returns (x / r, r) with r = sqrt(mean(x^2) + eps)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x / r, r
+
+
+def _prologue(x, positions, rope, rope_base, qk_norm, norm_eps):
+    """Raw rows -> the rows that enter the score product; also returns what the backward needs."""
+    y = rope_rotate(x, positions, rope_base) if rope else np.asarray(x, dtype=np.float64)
+    if qk_norm:
+        yhat, r = rms_normalize(y, norm_eps)
+    else:
+        yhat, r = y, None
+    return yhat, r
+
+
+def _prologue_backward(dyhat, yhat, r, positions, rope, rope_base, qk_norm):
+    """Gradient through the prologue: RMSNorm backward, then RoPE backward.
+
+    For yhat = y / r with r = sqrt(mean(y^2) + eps):  dy = (dyhat - yhat * mean(dyhat * yhat)) / r.
+    For y = R(a) x:  dx = R(a)^T dy = R(-a) dy.
+    """
+    if qk_norm:
+        dy = (dyhat - yhat * np.mean(dyhat * yhat, axis=-1, keepdims=True)) / r
+    else:
+        dy = dyhat
+    return rope_unrotate(dy, positions, rope_base) if rope else dy
+
+
+# --------------------------------------------------------------------------------------
+# Mask ("GPT pretraining" page, "Multihead Attention"; flaxchat "Core Features" window)
+# --------------------------------------------------------------------------------------
+def visible_mask(T: int, window: int = 0) -> np.ndarray:
+    """Boolean [T, T]: True where key j is visible to query i (j <= i, and i - j < window if window > 0)."""
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    m = j <= i
+    if window > 0:
+        m &= (i - j) < window
+    return m
+
+
+def _scores(qh, kh, scale, softcap):
+    """Scaled scores and their soft-capped version for one (b, h): both [Tq, Tk]."""
+    s_pre = scale * (qh @ kh.T)
+    if softcap > 0:
+        return s_pre, softcap * np.tanh(s_pre / softcap)
+    return s_pre, s_pre
+
+
+def _softmax_rows(s, allowed):
+    """Row softmax over the allowed entries (masked entries are -inf); also the natural-log LSE."""
+    s = np.where(allowed, s, -np.inf)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=-1, keepdims=True)
+    return e / l, (m + np.log(l))[..., 0]
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, Hq, T, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, T, d] matching q")
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, T, d
+
+
+def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
+                      rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+    """Causal attention forward for q [B,Hq,T,d], k/v [B,Hkv,T,d]; returns (O [B,Hq,T,d], LSE [B,Hq,T]).
+
+    Per (b, h):  q^ = prologue(q), k^ = prologue(k);  S = scale * q^ k^T;  S <- c tanh(S / c)
+    if capped;  masked entries -> -inf;  P = row softmax(S);  O = P V;  LSE = ln sum_j exp(S_ij).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(d)
+    group = Hq // Hkv
+    pos = np.arange(T)
+    allowed = visible_mask(T, window)
+    O = np.empty((B, Hq, T, d))
+    LSE = np.empty((B, Hq, T))
+    for b in range(B):
+        khat = [_prologue(k[b, g], pos, rope, rope_base, qk_norm, norm_eps)[0] for g in range(Hkv)]
+        for h in range(Hq):
+            g = h // group
+            qh, _ = _prologue(q[b, h], pos, rope, rope_base, qk_norm, norm_eps)
+            _, s = _scores(qh, khat[g], scale, softcap)
+            P, lse = _softmax_rows(s, allowed)
+            O[b, h] = P @ v[b, g]
+            LSE[b, h] = lse
+    return O, LSE
+
+
+def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=False,
+                       rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+    """Analytic gradients (dQ, dK, dV) of <O, dO> with respect to the RAW q, k, v.
+
+    Per (b, h) with g = kv head of h:
+      dV_g += P^T dO;  dP = dO V_g^T;  D_i = sum_d dO_i O_i;  dS = P * (dP - D);
+      dS_pre = dS * (1 - tanh(S_pre / c)^2) if capped;
+      dq^ = scale dS_pre k^;  dk^_g += scale dS_pre^T q^;
+    then each of dq^, dk^ goes back through RMSNorm and RoPE.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, Hq, Hkv, T, d = _check_shapes(q, k, v)
+    if dO.shape != q.shape:
+        raise ValueError("dO must have q's shape")
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(d)
+    group = Hq // Hkv
+    pos = np.arange(T)
+    allowed = visible_mask(T, window)
+    dQ = np.empty_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(B):
+        kpro = [_prologue(k[b, g], pos, rope, rope_base, qk_norm, norm_eps) for g in range(Hkv)]
+        dkhat = [np.zeros((T, d)) for _ in range(Hkv)]
+        for h in range(Hq):
+            g = h // group
+            qhat, rq = _prologue(q[b, h], pos, rope, rope_base, qk_norm, norm_eps)
+            khat = kpro[g][0]
+            s_pre, s = _scores(qhat, khat, scale, softcap)
+            P, _ = _softmax_rows(s, allowed)
+            O = P @ v[b, g]
+            dV[b, g] += P.T @ dO[b, h]
+            dP = dO[b, h] @ v[b, g].T
+            D = np.sum(dO[b, h] * O, axis=-1, keepdims=True)
+            dS = P * (dP - D)
+            if softcap > 0:
+                dS = dS * (1.0 - np.tanh(s_pre / softcap) ** 2)
+            dqhat = scale * (dS @ khat)
+            dkhat[g] += scale * (dS.T @ qhat)
+            dQ[b, h] = _prologue_backward(dqhat, qhat, rq, pos, rope, rope_base, qk_norm)
+        for g in range(Hkv):
+            khat, rk = kpro[g]
+            dK[b, g] = _prologue_backward(dkhat[g], khat, rk, pos, rope, rope_base, qk_norm)
+    return dQ, dK, dV
+
+
+def attention_decode(q, k_cache, v_cache, cache_len, *, softcap=0.0, scale=None, rope=False,
+                     rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+    """One-token decode: q [B,Hq,d] attends over the first L_b rows of k/v_cache [B,Hkv,Lmax,d].
+
+    The cached keys are taken as already rotated (and normalised, when QK-norm is on); only
+    the query is rotated, at position L_b - 1, and normalised.  cache_len is clamped to
+    [0, Lmax]; a sequence with L_b = 0 gives a zero output row.  Returns o [B,Hq,d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, Hq, d = q.shape
+    if kc.ndim != 4 or kc.shape != vc.shape or kc.shape[0] != B or kc.shape[3] != d:
+        raise ValueError("caches must be [B, Hkv, Lmax, d] matching q")
+    Hkv, Lmax = kc.shape[1], kc.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(d)
+    group = Hq // Hkv
+    o = np.zeros((B, Hq, d))
+    for b in range(B):
+        L = int(min(max(int(cache_len[b]), 0), Lmax))
+        if L == 0:
+            continue
+        qhat, _ = _prologue(q[b][:, None, :], np.array([L - 1]), rope, rope_base, qk_norm, norm_eps)
+        for h in range(Hq):
+            g = h // group
+            _, s = _scores(qhat[h], kc[b, g, :L], scale, softcap)
+            P, _ = _softmax_rows(s, np.ones_like(s, dtype=bool))
+            o[b, h] = (P @ vc[b, g, :L])[0]
+    return o

@@ -1,0 +1,381 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code.
+
+Each test checks the oracle against something other than itself: a per-query brute
+force written with scalar loops and complex-number RoPE, central finite differences,
+exact invariants of the attention definition, or special cases with a textbook answer.
+No GPU is needed.
+"""
+import cmath
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (attention_backward, attention_decode, attention_forward, rms_normalize,
+                    rope_rotate, rope_unrotate, visible_mask)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ------------------------------------------------------------------------------------
+# Brute force: one query at a time, scalar Python, RoPE as complex multiplication.
+# ------------------------------------------------------------------------------------
+def _bf_prologue(row, pos, rope, base, qk_norm, eps):
+    d = len(row)
+    half = d // 2
+    out = list(row)
+    if rope:
+        for i in range(half):
+            z = complex(row[i], row[i + half]) * cmath.exp(1j * pos * base ** (-2.0 * i / d))
+            out[i], out[i + half] = z.real, z.imag
+    if qk_norm:
+        ms = sum(x * x for x in out) / d
+        out = [x / math.sqrt(ms + eps) for x in out]
+    return out
+
+
+def brute_force_forward(q, k, v, window, softcap, rope, qk_norm, base=10000.0, eps=1e-6):
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, T, d))
+    L = np.zeros((B, Hq, T))
+    for b, h, i in itertools.product(range(B), range(Hq), range(T)):
+        g = h * Hkv // Hq
+        qi = _bf_prologue(q[b, h, i], i, rope, base, qk_norm, eps)
+        keys = [j for j in range(T) if j <= i and (window == 0 or i - j < window)]
+        scores = []
+        for j in keys:
+            kj = _bf_prologue(k[b, g, j], j, rope, base, qk_norm, eps)
+            s = scale * sum(a * c for a, c in zip(qi, kj))
+            if softcap:
+                s = softcap * math.tanh(s / softcap)
+            scores.append(s)
+        mx = max(scores)
+        w = [math.exp(s - mx) for s in scores]
+        tot = sum(w)
+        for jj, j in enumerate(keys):
+            O[b, h, i] += (w[jj] / tot) * v[b, g, j]
+        L[b, h, i] = mx + math.log(tot)
+    return O, L
+
+
+FLAG_SETS = [
+    dict(window=0, softcap=0.0, rope=False, qk_norm=False),
+    dict(window=0, softcap=0.5, rope=False, qk_norm=False),
+    dict(window=0, softcap=50.0, rope=True, qk_norm=True),
+    dict(window=2, softcap=0.0, rope=True, qk_norm=False),
+    dict(window=1, softcap=0.0, rope=False, qk_norm=True),
+    dict(window=3, softcap=0.5, rope=True, qk_norm=True),
+]
+
+
+@pytest.mark.parametrize("heads", [(1, 1), (2, 1), (4, 2), (3, 3)])
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_forward_matches_brute_force(heads, flags):
+    rng = np.random.default_rng(7)
+    Hq, Hkv = heads
+    for T, d in [(1, 2), (5, 4), (9, 8)]:
+        q, k, v = rnd(rng, 2, Hq, T, d), rnd(rng, 2, Hkv, T, d), rnd(rng, 2, Hkv, T, d)
+        O, L = attention_forward(q, k, v, **flags)
+        Ob, Lb = brute_force_forward(q, k, v, **flags)
+        np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, Lb, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# Finite differences for the analytic backward.
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_backward_matches_finite_differences(flags):
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, T, d = 1, 2, 1, 7, 8
+    q, k, v = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d)
+    dO = rnd(rng, B, Hq, T, d)
+    dQ, dK, dV = attention_backward(q, k, v, dO, **flags)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(attention_forward(q_, k_, v_, **flags)[0] * dO))
+
+    h = 1e-6
+    for name, x, grad in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{f"{n}_": a for n, a in args_p.items()})
+                        - loss(**{f"{n}_": a for n, a in args_m.items()})) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=0, atol=2e-7, err_msg=name)
+
+
+# ------------------------------------------------------------------------------------
+# Exact invariants of the definition.
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_rows_of_p_sum_to_one(flags):
+    rng = np.random.default_rng(3)
+    q, k = rnd(rng, 2, 4, 33, 8), rnd(rng, 2, 2, 33, 8)
+    O, _ = attention_forward(q, k, np.ones((2, 2, 33, 8)), **flags)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_causal_invariant(flags):
+    """Output row t does not change when tokens after t are perturbed."""
+    rng = np.random.default_rng(5)
+    T = 24
+    q, k, v = rnd(rng, 1, 2, T, 8), rnd(rng, 1, 1, T, 8), rnd(rng, 1, 1, T, 8)
+    O, L = attention_forward(q, k, v, **flags)
+    for t in (0, 5, 17):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        q2[:, :, t + 1:] += rnd(rng, 1, 2, T - t - 1, 8)
+        k2[:, :, t + 1:] *= 3.0
+        v2[:, :, t + 1:] -= 7.0
+        O2, L2 = attention_forward(q2, k2, v2, **flags)
+        np.testing.assert_allclose(O2[:, :, : t + 1], O[:, :, : t + 1], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(L2[:, :, : t + 1], L[:, :, : t + 1], rtol=0, atol=1e-14)
+        assert np.abs(O2[:, :, t + 1:] - O[:, :, t + 1:]).max() > 1e-3
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_gradient_sum_identities(flags):
+    """sum_j dV_j = sum_i dO_i per (b, kv head) over the group (rows of P sum to 1), and
+    <Q, dQ> = <K, dK> per (b, kv head) (scores are invariant to Q -> aQ, K -> K/a;
+    only exact without QK-norm, which breaks that scaling)."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, T, d = 2, 4, 2, 13, 8
+    q, k, v = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d)
+    dO = rnd(rng, B, Hq, T, d)
+    dQ, dK, dV = attention_backward(q, k, v, dO, **flags)
+    g = Hq // Hkv
+    np.testing.assert_allclose(dV.sum(axis=2),
+                               dO.reshape(B, Hkv, g, T, d).sum(axis=(2, 3)), rtol=0, atol=1e-12)
+    if not flags["qk_norm"]:
+        lhs = (q * dQ).reshape(B, Hkv, g, T, d).sum(axis=(2, 3, 4))
+        rhs = (k * dK).sum(axis=(2, 3))
+        np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12)
+    else:
+        # QK-norm: each normalised row is scale-invariant, so <x_row, dx_row> = O(eps).
+        assert np.abs((q * dQ).sum(-1)).max() < 1e-4
+        assert np.abs((k * dK).sum(-1)).max() < 1e-4
+
+
+def test_plain_attention_dk_sums_to_zero():
+    """Without RoPE/cap/norm, adding a constant vector to every key shifts each score row by a
+    constant, which softmax ignores: sum_j dK_j = 0."""
+    rng = np.random.default_rng(10)
+    q, k, v, dO = rnd(rng, 1, 2, 11, 4), rnd(rng, 1, 1, 11, 4), rnd(rng, 1, 1, 11, 4), rnd(rng, 1, 2, 11, 4)
+    _, dK, _ = attention_backward(q, k, v, dO)
+    np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------
+# Special cases with textbook answers.
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_single_token_returns_value(flags):
+    rng = np.random.default_rng(1)
+    q, k, v = rnd(rng, 3, 2, 1, 8), rnd(rng, 3, 1, 1, 8), rnd(rng, 3, 1, 1, 8)
+    O, _ = attention_forward(q, k, v, **flags)
+    np.testing.assert_allclose(O, np.repeat(v, 2, axis=1), atol=1e-15)
+
+
+def test_window_one_is_identity():
+    rng = np.random.default_rng(2)
+    q, k, v, dO = rnd(rng, 2, 2, 9, 8), rnd(rng, 2, 2, 9, 8), rnd(rng, 2, 2, 9, 8), rnd(rng, 2, 2, 9, 8)
+    for rope, norm, cap in itertools.product([0, 1], [0, 1], [0.0, 2.0]):
+        kw = dict(window=1, rope=bool(rope), qk_norm=bool(norm), softcap=cap)
+        O, L = attention_forward(q, k, v, **kw)
+        np.testing.assert_allclose(O, v, atol=1e-15)
+        dQ, dK, dV = attention_backward(q, k, v, dO, **kw)
+        np.testing.assert_allclose(dQ, 0.0, atol=1e-14)
+        np.testing.assert_allclose(dK, 0.0, atol=1e-14)
+        np.testing.assert_allclose(dV, dO, atol=1e-14)
+
+
+def test_zero_query_gives_prefix_mean():
+    """q = 0 makes every visible score equal, so row t is the mean of v_0..v_t (window: of the
+    last W rows)."""
+    rng = np.random.default_rng(4)
+    T = 10
+    q, k, v = np.zeros((1, 2, T, 4)), rnd(rng, 1, 2, T, 4), rnd(rng, 1, 2, T, 4)
+    for window, rope, norm in [(0, False, False), (0, True, True), (3, True, False)]:
+        O, L = attention_forward(q, k, v, window=window, rope=rope, qk_norm=norm, softcap=5.0)
+        for t in range(T):
+            lo = 0 if window == 0 else max(0, t - window + 1)
+            np.testing.assert_allclose(O[0, :, t], v[0, :, lo: t + 1].mean(axis=1), atol=1e-14)
+            np.testing.assert_allclose(L[0, :, t], math.log(t + 1 - lo), atol=1e-14)
+
+
+def test_two_token_closed_form():
+    """T = 2, d = 2, plain attention: row 1 is the logistic mix of v_0 and v_1."""
+    q = np.array([[[[0.3, -1.2], [0.8, 0.5]]]])
+    k = np.array([[[[1.5, 0.25], [-0.5, 2.0]]]])
+    v = np.array([[[[1.0, -2.0], [4.0, 3.0]]]])
+    O, L = attention_forward(q, k, v)
+    s0 = (0.8 * 1.5 + 0.5 * 0.25) / math.sqrt(2)
+    s1 = (0.8 * -0.5 + 0.5 * 2.0) / math.sqrt(2)
+    p1 = 1.0 / (1.0 + math.exp(s0 - s1))
+    np.testing.assert_allclose(O[0, 0, 0], v[0, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(O[0, 0, 1], (1 - p1) * v[0, 0, 0] + p1 * v[0, 0, 1], atol=1e-15)
+    np.testing.assert_allclose(L[0, 0, 1], math.log(math.exp(s0) + math.exp(s1)), atol=1e-15)
+
+
+def test_large_window_equals_causal_and_large_cap_equals_none():
+    rng = np.random.default_rng(6)
+    q, k, v, dO = rnd(rng, 1, 2, 12, 8), rnd(rng, 1, 1, 12, 8), rnd(rng, 1, 1, 12, 8), rnd(rng, 1, 2, 12, 8)
+    base = attention_forward(q, k, v, rope=True)
+    for a, b in zip(attention_forward(q, k, v, rope=True, window=12), base):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(attention_forward(q, k, v, rope=True, window=40), base):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(attention_forward(q, k, v, rope=True, softcap=1e7), base):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+    for a, b in zip(attention_backward(q, k, v, dO, rope=True, softcap=1e7),
+                    attention_backward(q, k, v, dO, rope=True)):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_gqa_equals_mha_with_repeated_kv(flags):
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, T, d = 2, 6, 2, 9, 4
+    q, k, v, dO = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hq, T, d)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    Og, Lg = attention_forward(q, k, v, **flags)
+    Om, Lm = attention_forward(q, kr, vr, **flags)
+    np.testing.assert_allclose(Og, Om, atol=1e-14)
+    np.testing.assert_allclose(Lg, Lm, atol=1e-14)
+    dQg, dKg, dVg = attention_backward(q, k, v, dO, **flags)
+    dQm, dKm, dVm = attention_backward(q, kr, vr, dO, **flags)
+    np.testing.assert_allclose(dQg, dQm, atol=1e-13)
+    np.testing.assert_allclose(dKg, dKm.reshape(B, Hkv, 3, T, d).sum(axis=2), atol=1e-13)
+    np.testing.assert_allclose(dVg, dVm.reshape(B, Hkv, 3, T, d).sum(axis=2), atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------
+# Prologue pieces: RoPE and RMSNorm.
+# ------------------------------------------------------------------------------------
+def test_rope_properties():
+    rng = np.random.default_rng(12)
+    d, T = 16, 50
+    x = rnd(rng, T, d)
+    pos = np.arange(T)
+    y = rope_rotate(x, pos)
+    np.testing.assert_allclose(y[0], x[0], atol=0)                                # p = 0
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    np.testing.assert_allclose(rope_unrotate(y, pos), x, atol=1e-14)
+    # First pair turns by exactly p radians, the last by p * base^(-(d-2)/d).
+    e = np.zeros((1, d))
+    e[0, 0] = 1.0
+    for p in (1, 7, 2047):
+        r = rope_rotate(e, np.array([p]))[0]
+        assert abs(r[0] - math.cos(p)) < 1e-12 and abs(r[d // 2] - math.sin(p)) < 1e-12
+    e = np.zeros((1, d))
+    e[0, d // 2 - 1] = 1.0
+    w = 10000.0 ** (-(d - 2) / d)
+    r = rope_rotate(e, np.array([3]))[0]
+    assert abs(r[d // 2 - 1] - math.cos(3 * w)) < 1e-14 and abs(r[d - 1] - math.sin(3 * w)) < 1e-14
+    # Scores depend only on the offset between positions.
+    a, b = rnd(rng, 1, d), rnd(rng, 1, d)
+    for p1, p2, shift in [(5, 2, 11), (40, 0, 3), (9, 9, 100)]:
+        s = (rope_rotate(a, np.array([p1])) @ rope_rotate(b, np.array([p2])).T)[0, 0]
+        s2 = (rope_rotate(a, np.array([p1 + shift])) @ rope_rotate(b, np.array([p2 + shift])).T)[0, 0]
+        assert abs(s - s2) < 1e-12
+
+
+def test_rope_and_norm_commute_and_norm_value():
+    rng = np.random.default_rng(13)
+    x = rnd(rng, 30, 8) * 3.0
+    pos = np.arange(30)
+    eps = 1e-6
+    a, _ = rms_normalize(rope_rotate(x, pos), eps)
+    b = rope_rotate(rms_normalize(x, eps)[0], pos)
+    np.testing.assert_allclose(a, b, atol=1e-14)
+    y, r = rms_normalize(x, eps)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), ms / (ms + eps), rtol=1e-14)
+    np.testing.assert_allclose(r[:, 0], np.sqrt(ms + eps), rtol=1e-15)
+
+
+def test_mask_matches_page_conventions():
+    """MiniGPT builds the allowed set as the lower triangle of ones; the GPT pretraining page masks
+    the strict upper triangle; the KV-cache offset mask with q_len == k_len is the same mask."""
+    T = 7
+    m = visible_mask(T)
+    np.testing.assert_array_equal(m, np.tril(np.ones((T, T))).astype(bool))
+    np.testing.assert_array_equal(~m, np.triu(np.ones((T, T), dtype=bool), 1))
+    rows, cols = np.arange(T)[:, None], np.arange(T)[None, :]
+    np.testing.assert_array_equal(~m, cols > (0 + rows))
+    for W in (1, 2, 5):
+        np.testing.assert_array_equal(visible_mask(T, W).sum(axis=1), np.minimum(np.arange(T) + 1, W))
+
+
+# ------------------------------------------------------------------------------------
+# Decode.
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", [dict(softcap=0.0, rope=False, qk_norm=False),
+                                   dict(softcap=50.0, rope=True, qk_norm=False),
+                                   dict(softcap=2.0, rope=True, qk_norm=True)])
+def test_decode_equals_last_row_of_forward(flags):
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, T, d = 3, 4, 2, 15, 8
+    q, k, v = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d)
+    pos = np.arange(T)
+    kc = rope_rotate(k, pos) if flags["rope"] else k.copy()
+    if flags["qk_norm"]:
+        kc = rms_normalize(kc)[0]
+    Lmax = T + 4
+    kcache = np.full((B, Hkv, Lmax, d), np.nan)
+    vcache = np.full((B, Hkv, Lmax, d), np.nan)
+    lens = np.array([T, 1, 9])
+    for b in range(B):
+        kcache[b, :, :T] = kc[b]
+        vcache[b, :, :T] = v[b]
+    assert attention_decode(q[:, :, -1], kcache, vcache, lens, **flags).shape == (B, Hq, d)
+    for b in range(B):
+        L = lens[b]
+        O, _ = attention_forward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], **flags)
+        ob = attention_decode(q[b:b + 1, :, L - 1], kcache[b:b + 1], vcache[b:b + 1], lens[b:b + 1], **flags)
+        np.testing.assert_allclose(ob[0], O[0, :, L - 1], atol=1e-14)
+
+
+def test_decode_zero_length_and_clamp():
+    rng = np.random.default_rng(15)
+    q, kc, vc = rnd(rng, 3, 2, 4), rnd(rng, 3, 1, 6, 4), rnd(rng, 3, 1, 6, 4)
+    o = attention_decode(q, kc, vc, np.array([0, -5, 99]))
+    np.testing.assert_array_equal(o[0], 0.0)
+    np.testing.assert_array_equal(o[1], 0.0)
+    o_full = attention_decode(q[2:], kc[2:], vc[2:], np.array([6]))
+    np.testing.assert_allclose(o[2], o_full[0], atol=0)
+
+
+# ------------------------------------------------------------------------------------
+# Workload shapes come from the pages.
+# ------------------------------------------------------------------------------------
+def test_workload_shapes_match_pages():
+    from causal_attention_02_amd.inputs import WORKLOADS
+    ps = json.load(open(os.path.join(GOLDEN, "page_shapes.json")))
+    mg, nano, fc = ps["minigpt"], ps["nanogpt_181m"], ps["flaxchat_depth12"]
+    w = WORKLOADS["minigpt_fwd_f32"]
+    assert (w.T, w.Hq, w.D) == (mg["maxlen"], mg["num_heads"], mg["embed_dim"] // mg["num_heads"])
+    w = WORKLOADS["minigpt_train_bf16"]
+    assert (w.B, w.T, w.Hq, w.D) == (mg["batch_size"], mg["maxlen"], mg["num_heads"], 32)
+    for name in ("gqa181m_train", "gqa181m_decode"):
+        w = WORKLOADS[name]
+        assert (w.Hq, w.Hkv, w.D, w.T) == (nano["query_heads"], nano["kv_heads"], nano["head_dim"],
+                                           nano["sequence_length"])
+    for name in ("flaxchat_full", "flaxchat_w512"):
+        w = WORKLOADS[name]
+        assert (w.Hq, w.Hkv, w.D) == (fc["heads"], fc["kv_heads"], fc["model_dim"] // fc["heads"])
