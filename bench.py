@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = attn_fwd + attn_bwd on the 181M-style GQA workload (B=16, T=2048, 8 query / 4 KV
+heads, d=96, causal, RoPE, QK-norm, soft-cap 50), inputs resident in HBM.  The printed JSON
+line's `value` is that step's algorithmic throughput in TFLOP/s (14 d flops per visible
+(query, key) pair).  The same line also reports:
+  * decode: KV-cache decode of 64 sequences (cache lengths U{256..2048}, 8/4 heads, d=96,
+    RoPE, soft-cap 50) in GB/s of active K/V read, rotating over several cache copies so the
+    last-level cache cannot serve them;
+  * the flaxchat-style d=128 workloads (full causal and window 512) fwd+bwd;
+  * roofline: the dominant kernel's algorithmic rate against the MI355X bf16 dense peak,
+    from per-kernel HIP events recorded by the library's trace on the launch stream;
+  * cpu_baseline: the fp64 numpy oracle on a bounded sample of the same workload.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "causal attn fwd+bwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=200)
+    ap.add_argument("--decode-copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["train", "decode", "all"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from causal_attention_02_amd import binding as bd
+    from causal_attention_02_amd.inputs import (WORKLOADS, decode_bytes, make_decode_inputs,
+                                                make_train_inputs, train_flops, visible_pairs)
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.lib()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    stream = torch.cuda.current_stream()
+
+    def opts_of(w):
+        return bd.AttnOptions(window=w.window, softcap=w.softcap, rope=w.rope,
+                              rope_base=w.rope_base, qk_norm=w.qk_norm, norm_eps=w.norm_eps)
+
+    def to_dev(x):
+        return torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
+
+    # ------------------------------------------------------------------------------------
+    # fwd + bwd
+    # ------------------------------------------------------------------------------------
+    def train_case(w, steps, warmup, trace=False):
+        q, k, v, dO = make_train_inputs(w)
+        tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(dO)
+        del q, k, v, dO
+        o = torch.empty_like(tq)
+        lse = torch.empty(tq.shape[:3], dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        opts = opts_of(w)
+        B, Hq, T, D = tq.shape
+        Hkv = tk.shape[1]
+        wsf = torch.empty(max(bd.fwd_workspace_bytes(B, T, Hq, Hkv, D, opts), 1), dtype=torch.uint8,
+                          device=dev)
+        wsb = torch.empty(max(bd.bwd_workspace_bytes(B, T, Hq, Hkv, D, opts), 1), dtype=torch.uint8,
+                          device=dev)
+
+        def step():
+            bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf)
+            bd.attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+        total_ms = ev[0].elapsed_time(ev[steps])
+        kern = None
+        if trace:
+            bd.trace_enable(True)
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            kern = bd.trace_read()
+            bd.trace_enable(False)
+        return total_ms / steps, per, kern
+
+    result = {}
+    extra = {}
+    main_w = WORKLOADS["gqa181m_train"]
+    if args.only in ("train", "all"):
+        log(f"[bench] fwd+bwd {main_w.name}: steps={args.steps} warmup={args.warmup}")
+        ms, per, kern = train_case(main_w, args.steps, args.warmup, trace=True)
+        flops = train_flops(main_w)
+        tflops = flops / (ms * 1e-3) / 1e12
+        result.update(value=tflops, ms_per_step=ms)
+        extra["gqa181m_train"] = dict(ms_median=float(np.median(per)),
+                                      ms_p90=float(np.percentile(per, 90)),
+                                      tflops=tflops, pct_peak=100 * tflops / PEAK_BF16_TFLOPS)
+        log(f"[bench] {main_w.name}: {ms:.3f} ms/step  {tflops:.1f} TFLOP/s")
+        # Dominant kernel and its algorithmic rate.
+        pairs = visible_pairs(main_w.T, main_w.window) * main_w.B * main_w.Hq
+        algo_per_pair = {"fwd_bf16": 4 * main_w.D, "bwd_dkdv": 8 * main_w.D, "bwd_dq": 2 * main_w.D}
+        kern_ms = {n: (c, t / c) for n, (c, t) in kern.items()}
+        extra["kernels_ms"] = {n: round(a, 4) for n, (c, a) in kern_ms.items()}
+        dom = max(kern.items(), key=lambda kv: kv[1][1])[0]
+        fam = next((f for f in algo_per_pair if dom.startswith(f)), None)
+        avg_ms = kern_ms[dom][1]
+        roof = {"kernel": dom, "avg_ms": avg_ms}
+        if fam is not None:
+            achieved = algo_per_pair[fam] * pairs / (avg_ms * 1e-3) / 1e12
+            roof.update(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=achieved / PEAK_BF16_TFLOPS, traffic=None,
+                        algorithmic_flops_per_launch=algo_per_pair[fam] * pairs)
+        result["roofline"] = roof
+        for name in ("flaxchat_full", "flaxchat_w512"):
+            w = WORKLOADS[name]
+            log(f"[bench] fwd+bwd {name}")
+            ms2, per2, _ = train_case(w, max(args.steps // 2, 3), 2)
+            tf2 = train_flops(w) / (ms2 * 1e-3) / 1e12
+            extra[name] = dict(ms_per_step=ms2, ms_median=float(np.median(per2)), tflops=tf2,
+                               pct_peak=100 * tf2 / PEAK_BF16_TFLOPS)
+            log(f"[bench] {name}: {ms2:.3f} ms/step  {tf2:.1f} TFLOP/s")
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------------------------
+    # decode
+    # ------------------------------------------------------------------------------------
+    if args.only in ("decode", "all"):
+        wd = WORKLOADS["gqa181m_decode"]
+        log(f"[bench] decode {wd.name}: {args.decode_iters} calls over {args.decode_copies} cache copies")
+        qd, kc, vc, lens = make_decode_inputs(wd)
+        tq = to_dev(qd)
+        tkc0, tvc0 = to_dev(kc), to_dev(vc)
+        del kc, vc
+        copies = [(tkc0, tvc0)] + [(tkc0.clone(), tvc0.clone()) for _ in range(args.decode_copies - 1)]
+        tl = torch.from_numpy(lens).to(dev)
+        od = torch.empty_like(tq)
+        opts = opts_of(wd)
+        cfg = bd.make_decode_cfg(wd.B, wd.Hq, wd.Hkv, wd.D, wd.T, opts)
+        import ctypes
+        wsd = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg))),
+                          dtype=torch.uint8, device=dev)
+        for i in range(10):
+            kcc, vcc = copies[i % len(copies)]
+            bd.attn_decode(tq, kcc, vcc, tl, opts, out=od, workspace=wsd)
+        torch.cuda.synchronize()
+        n = args.decode_iters
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
+            kcc, vcc = copies[i % len(copies)]
+            bd.attn_decode(tq, kcc, vcc, tl, opts, out=od, workspace=wsd)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+        ms_d = ev[0].elapsed_time(ev[n]) / n
+        nbytes = decode_bytes(wd, lens)
+        gbs = nbytes / (ms_d * 1e-3) / 1e9
+        bd.trace_enable(True)
+        for i in range(n):
+            kcc, vcc = copies[i % len(copies)]
+            bd.attn_decode(tq, kcc, vcc, tl, opts, out=od, workspace=wsd)
+        torch.cuda.synchronize()
+        dk = bd.trace_read()
+        bd.trace_enable(False)
+        split = {k: round(t / c, 5) for k, (c, t) in dk.items()}
+        extra["decode"] = dict(ms_per_call=ms_d, ms_median=float(np.median(per)),
+                               ms_p90=float(np.percentile(per, 90)), GBps=gbs,
+                               pct_hbm_peak=100 * gbs / PEAK_HBM_GBS, bytes_per_call=nbytes,
+                               kernels_ms=split)
+        log(f"[bench] decode: {ms_d * 1e3:.1f} us/call  {gbs:.0f} GB/s")
+        if "value" not in result:
+            result.update(value=gbs, ms_per_step=ms_d)
+
+    # ------------------------------------------------------------------------------------
+    # CPU oracle on a bounded sample
+    # ------------------------------------------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline and args.only in ("train", "all"):
+        from oracle import attention_backward, attention_forward
+        w = main_w
+        q, k, v, dO = make_train_inputs(w)
+        G = w.Hq // w.Hkv
+        kw = dict(window=w.window, softcap=w.softcap, rope=w.rope, rope_base=w.rope_base,
+                  qk_norm=w.qk_norm, norm_eps=w.norm_eps)
+        t0 = time.perf_counter()
+        units = 0
+        while True:
+            b, g = units % w.B, (units // w.B) % w.Hkv
+            hs = slice(g * G, (g + 1) * G)
+            attention_forward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], **kw)
+            attention_backward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                               dO[b:b + 1, hs], **kw)
+            units += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        sample_flops = train_flops(w.with_(B=1, Hq=G, Hkv=1)) * units
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count()
+        cpu = {"value": sample_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{units} (batch, KV-group) slices of {w.name} (1 x {G} query heads x "
+                         f"T={w.T} x d={w.D}) fwd+bwd in {el:.1f} s, host os.cpu_count()="
+                         f"{os.cpu_count()}"}
+        log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s over {units} slices")
+
+    line = {
+        "metric": METRIC,
+        "value": result.get("value"),
+        "unit": "TFLOP/s" if args.only in ("train", "all") else "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": result.get("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{main_w.name}: fwd+bwd, B={main_w.B} T={main_w.T} Hq={main_w.Hq} "
+                               f"Hkv={main_w.Hkv} d={main_w.D} causal RoPE QK-norm softcap "
+                               f"{main_w.softcap:g}",
+                   "global_batch": main_w.B, "seq_len": main_w.T, "parallelism": "single GPU"},
+        "pct_of_peak": (100 * result["value"] / PEAK_BF16_TFLOPS
+                        if args.only in ("train", "all") and result.get("value") else None),
+        "device": {"name": props.name, "cu": props.multi_processor_count},
+        "roofline": result.get("roofline"),
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

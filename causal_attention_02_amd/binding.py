@@ -1,0 +1,275 @@
+"""ctypes binding of libcausal_attn.so (argument marshalling only).
+
+Every step of the attention path runs in the library's HIP kernels; this module only checks
+tensor shapes/dtypes, allocates outputs and workspaces with PyTorch (device memory) and
+passes raw pointers plus the current HIP stream to the C ABI declared in include/attn.h.
+If the library is missing, every entry point raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libcausal_attn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_ELAUNCH = 0, -1, -2, -3, -4
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTED = [
+    "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes",
+    "attn_check_cfg", "attn_check_decode_cfg", "attn_fwd", "attn_bwd", "attn_decode",
+    "attn_status_str", "attn_trace_enable", "attn_trace_read",
+]
+
+
+class AttnCfg(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("softcap", ctypes.c_float), ("scale", ctypes.c_float), ("rope", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("qk_norm", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class AttnDecodeCfg(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("Lmax", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("scale", ctypes.c_float), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("qk_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("split_len", ctypes.c_int32)]
+
+
+class AttnTraceEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcausal_attn.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m causal_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        cfgp, dcfgp = ctypes.POINTER(AttnCfg), ctypes.POINTER(AttnDecodeCfg)
+        L.attn_fwd_workspace_bytes.argtypes = [cfgp]
+        L.attn_fwd_workspace_bytes.restype = sz
+        L.attn_bwd_workspace_bytes.argtypes = [cfgp]
+        L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_decode_workspace_bytes.argtypes = [dcfgp]
+        L.attn_decode_workspace_bytes.restype = sz
+        L.attn_check_cfg.argtypes = [cfgp, ctypes.c_int]
+        L.attn_check_cfg.restype = ctypes.c_int
+        L.attn_check_decode_cfg.argtypes = [dcfgp]
+        L.attn_check_decode_cfg.restype = ctypes.c_int
+        L.attn_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_bwd.restype = ctypes.c_int
+        L.attn_decode.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_decode.restype = ctypes.c_int
+        L.attn_status_str.argtypes = [ctypes.c_int]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_trace_enable.argtypes = [ctypes.c_int]
+        L.attn_trace_enable.restype = ctypes.c_int
+        L.attn_trace_read.argtypes = [ctypes.POINTER(AttnTraceEntry), ctypes.c_int]
+        L.attn_trace_read.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != ATTN_OK:
+        raise AttnError(status, what)
+
+
+@dataclass
+class AttnOptions:
+    """Variant flags shared by forward and backward (see attn_cfg in include/attn.h)."""
+    window: int = 0
+    softcap: float = 0.0
+    scale: float = 0.0
+    rope: bool = False
+    rope_base: float = 10000.0
+    qk_norm: bool = False
+    norm_eps: float = 1e-6
+
+
+def make_cfg(B, T, Hq, Hkv, D, opts: AttnOptions, dtype: int) -> AttnCfg:
+    return AttnCfg(B, T, Hq, Hkv, D, int(opts.window), float(opts.softcap), float(opts.scale),
+                   int(bool(opts.rope)), float(opts.rope_base), int(bool(opts.qk_norm)),
+                   float(opts.norm_eps), int(dtype))
+
+
+def make_decode_cfg(B, Hq, Hkv, D, Lmax, opts: AttnOptions, split_len: int = 0) -> AttnDecodeCfg:
+    return AttnDecodeCfg(B, Hq, Hkv, D, Lmax, float(opts.softcap), float(opts.scale),
+                         int(bool(opts.rope)), float(opts.rope_base), int(bool(opts.qk_norm)),
+                         float(opts.norm_eps), int(split_len))
+
+
+# ---------------------------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous GPU tensor")
+
+
+def _workspace(nbytes, device, ws):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {nbytes} needed")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def fwd_workspace_bytes(B, T, Hq, Hkv, D, opts: AttnOptions, dtype=ATTN_BF16) -> int:
+    return int(lib().attn_fwd_workspace_bytes(ctypes.byref(make_cfg(B, T, Hq, Hkv, D, opts, dtype))))
+
+
+def bwd_workspace_bytes(B, T, Hq, Hkv, D, opts: AttnOptions) -> int:
+    return int(lib().attn_bwd_workspace_bytes(ctypes.byref(make_cfg(B, T, Hq, Hkv, D, opts, ATTN_BF16))))
+
+
+def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, workspace=None,
+             stream=None):
+    """Forward: q [B,Hq,T,D], k/v [B,Hkv,T,D] (bf16 or fp32) -> (o, lse fp32 [B,Hq,T])."""
+    torch = _torch()
+    opts = opts or AttnOptions()
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype_code(q)
+    _need(q, (B, Hq, T, D), q.dtype, "q")
+    _need(k, (B, Hkv, T, D), q.dtype, "k")
+    _need(v, (B, Hkv, T, D), q.dtype, "v")
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, q.shape, q.dtype, "out")
+    _need(lse_t, (B, Hq, T), torch.float32, "lse")
+    cfg = make_cfg(B, T, Hq, Hkv, D, opts, dt)
+    st = lib().attn_check_cfg(ctypes.byref(cfg), 0)
+    _check(st, "attn_fwd")
+    ws = _workspace(int(lib().attn_fwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+    st = lib().attn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(ws),
+                        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+                        _stream(stream))
+    _check(st, "attn_fwd")
+    return o, lse_t
+
+
+def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Backward (bf16): returns (dq, dk, dv) with respect to the raw q, k, v."""
+    torch = _torch()
+    opts = opts or AttnOptions()
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    bf = torch.bfloat16
+    for t, shp, name in ((q, (B, Hq, T, D), "q"), (k, (B, Hkv, T, D), "k"), (v, (B, Hkv, T, D), "v"),
+                         (o, (B, Hq, T, D), "o"), (dO, (B, Hq, T, D), "dO")):
+        _need(t, shp, bf, name)
+    _need(lse, (B, Hq, T), torch.float32, "lse")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, q.shape, bf, "dq")
+    _need(dk, k.shape, bf, "dk")
+    _need(dv, v.shape, bf, "dv")
+    cfg = make_cfg(B, T, Hq, Hkv, D, opts, ATTN_BF16)
+    _check(lib().attn_check_cfg(ctypes.byref(cfg), 1), "attn_bwd")
+    ws = _workspace(int(lib().attn_bwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+    st = lib().attn_bwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+                        _stream(stream))
+    _check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None, *, split_len=0,
+                out=None, workspace=None, stream=None):
+    """Decode (bf16): q [B,Hq,D], caches [B,Hkv,Lmax,D], cache_len int32 [B] -> o [B,Hq,D]."""
+    torch = _torch()
+    opts = opts or AttnOptions()
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    bf = torch.bfloat16
+    _need(q, (B, Hq, D), bf, "q")
+    _need(k_cache, (B, Hkv, Lmax, D), bf, "k_cache")
+    _need(v_cache, (B, Hkv, Lmax, D), bf, "v_cache")
+    _need(cache_len, (B,), torch.int32, "cache_len")
+    o = torch.empty_like(q) if out is None else out
+    _need(o, q.shape, bf, "out")
+    cfg = make_decode_cfg(B, Hq, Hkv, D, Lmax, opts, split_len)
+    _check(lib().attn_check_decode_cfg(ctypes.byref(cfg)), "attn_decode")
+    ws = _workspace(int(lib().attn_decode_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+    st = lib().attn_decode(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len),
+                           _ptr(o), _ptr(ws),
+                           ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+                           _stream(stream))
+    _check(st, "attn_decode")
+    return o
+
+
+def trace_enable(on: bool = True):
+    _check(lib().attn_trace_enable(1 if on else 0), "attn_trace_enable")
+
+
+def trace_read() -> dict:
+    """{kernel name: (launches, total_ms)} recorded since trace_enable(True)."""
+    L = lib()
+    n = L.attn_trace_read(None, 0)
+    if n < 0:
+        raise AttnError(n, "attn_trace_read")
+    buf = (AttnTraceEntry * max(n, 1))()
+    n = L.attn_trace_read(buf, n)
+    if n < 0:
+        raise AttnError(n, "attn_trace_read")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}

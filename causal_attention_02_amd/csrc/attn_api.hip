@@ -1,0 +1,305 @@
+// C ABI of the attention library: argument validation, workspace layout, launch order and
+// the optional kernel trace.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------------------
+// Kernel trace
+// ---------------------------------------------------------------------------------------
+namespace {
+struct TraceRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct Tracer {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TraceRec> recs;
+};
+Tracer& tracer() {
+  static Tracer t;
+  return t;
+}
+void trace_clear_locked(Tracer& t) {
+  for (auto& r : t.recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  t.recs.clear();
+}
+}  // namespace
+
+TraceScope::TraceScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (!t.on) return;
+  TraceRec r{name, nullptr, nullptr};
+  if (hipEventCreate(&r.start) != hipSuccess) return;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return;
+  }
+  (void)hipEventRecord(r.start, s);
+  t.recs.push_back(r);
+  slot = (int)t.recs.size() - 1;
+}
+
+TraceScope::~TraceScope() {
+  if (slot < 0) return;
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (slot < (int)t.recs.size()) (void)hipEventRecord(t.recs[slot].stop, stream);
+}
+
+}  // namespace attn
+
+using namespace attn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool supported_d(int D) { return D == 32 || D == 64 || D == 96 || D == 128; }
+
+int check_cfg(const attn_cfg* c, int bwd) {
+  if (!c) return ATTN_EINVAL;
+  if (c->B < 0 || c->T < 0 || c->Hq < 1 || c->Hkv < 1 || c->Hq % c->Hkv != 0) return ATTN_EINVAL;
+  if (c->window < 0) return ATTN_EINVAL;
+  if (!(c->softcap >= 0.f) || !isfinite(c->softcap)) return ATTN_EINVAL;
+  if (!(c->scale >= 0.f) || !isfinite(c->scale)) return ATTN_EINVAL;
+  if (c->rope != 0 && c->rope != 1) return ATTN_EINVAL;
+  if (c->rope && (!(c->rope_base > 0.f) || !isfinite(c->rope_base))) return ATTN_EINVAL;
+  if (c->qk_norm != 0 && c->qk_norm != 1) return ATTN_EINVAL;
+  if (c->qk_norm && (!(c->norm_eps > 0.f) || !isfinite(c->norm_eps))) return ATTN_EINVAL;
+  if (c->dtype != ATTN_F32 && c->dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (c->D <= 0) return ATTN_EINVAL;
+  if (!supported_d(c->D)) return ATTN_EUNSUPPORTED;
+  if (bwd && c->dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  // Element offsets are 64-bit; row indices inside a (b, h) slice are 32-bit.
+  if ((int64_t)c->T * c->D > INT32_MAX) return ATTN_EUNSUPPORTED;
+  if ((int64_t)c->B * c->Hq > INT32_MAX / 64) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_dcfg(const attn_decode_cfg* c) {
+  if (!c) return ATTN_EINVAL;
+  if (c->B < 0 || c->Lmax < 0 || c->Hq < 1 || c->Hkv < 1 || c->Hq % c->Hkv != 0) return ATTN_EINVAL;
+  if (!(c->softcap >= 0.f) || !isfinite(c->softcap)) return ATTN_EINVAL;
+  if (!(c->scale >= 0.f) || !isfinite(c->scale)) return ATTN_EINVAL;
+  if (c->rope != 0 && c->rope != 1) return ATTN_EINVAL;
+  if (c->rope && (!(c->rope_base > 0.f) || !isfinite(c->rope_base))) return ATTN_EINVAL;
+  if (c->qk_norm != 0 && c->qk_norm != 1) return ATTN_EINVAL;
+  if (c->qk_norm && (!(c->norm_eps > 0.f) || !isfinite(c->norm_eps))) return ATTN_EINVAL;
+  if (c->split_len < 0 || c->split_len % 64 != 0) return ATTN_EINVAL;
+  if (c->D <= 0) return ATTN_EINVAL;
+  if (!supported_d(c->D)) return ATTN_EUNSUPPORTED;
+  if ((int64_t)c->Lmax * c->D > INT32_MAX) return ATTN_EUNSUPPORTED;
+  if ((int64_t)c->B * c->Hkv * c->Hq > (int64_t)UINT16_MAX * 1024) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
+
+int decode_split_len(const attn_decode_cfg* c) { return c->split_len > 0 ? c->split_len : 256; }
+
+int decode_nsplit(const attn_decode_cfg* c) {
+  const int sl = decode_split_len(c);
+  return c->Lmax > 0 ? (c->Lmax + sl - 1) / sl : 1;
+}
+
+// Workspace layouts (each region 256-byte aligned):
+//   fwd: [q^ B*Hq*T*D elt][k^ B*Hkv*T*D elt]                      when rope or qk_norm
+//   bwd: [D B*Hq*T f32] + when rope or qk_norm:
+//        [q^ bf16][k^ bf16][dq^ f32 B*Hq*T*D][dk^ f32 B*Hkv*T*D]
+size_t fwd_ws(const attn_cfg* c) {
+  if (!(c->rope || c->qk_norm)) return 0;
+  const size_t elt = c->dtype == ATTN_BF16 ? 2 : 4;
+  const size_t nq = (size_t)c->B * c->Hq * c->T * c->D, nk = (size_t)c->B * c->Hkv * c->T * c->D;
+  return align_up(nq * elt) + align_up(nk * elt);
+}
+
+size_t bwd_ws(const attn_cfg* c) {
+  const size_t rows = (size_t)c->B * c->Hq * c->T;
+  size_t s = align_up(rows * 4);
+  if (c->rope || c->qk_norm) {
+    const size_t nq = rows * c->D, nk = (size_t)c->B * c->Hkv * c->T * c->D;
+    s += align_up(nq * 2) + align_up(nk * 2) + align_up(nq * 4) + align_up(nk * 4);
+  }
+  return s;
+}
+
+size_t dec_ws(const attn_decode_cfg* c) {
+  return align_up((size_t)c->B * c->Hq * decode_nsplit(c) * (c->D + 2) * 4);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration";
+    case ATTN_EWORKSPACE: return "workspace missing or too small";
+    case ATTN_ELAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int attn_check_cfg(const attn_cfg* cfg, int for_backward) { return check_cfg(cfg, for_backward); }
+int attn_check_decode_cfg(const attn_decode_cfg* cfg) { return check_dcfg(cfg); }
+
+size_t attn_fwd_workspace_bytes(const attn_cfg* cfg) {
+  return check_cfg(cfg, 0) == ATTN_OK ? fwd_ws(cfg) : 0;
+}
+size_t attn_bwd_workspace_bytes(const attn_cfg* cfg) {
+  return check_cfg(cfg, 1) == ATTN_OK ? bwd_ws(cfg) : 0;
+}
+size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg) {
+  return check_dcfg(cfg) == ATTN_OK ? dec_ws(cfg) : 0;
+}
+
+int attn_fwd(const attn_cfg* c, const void* q, const void* k, const void* v, void* o, float* lse,
+             void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(c, 0);
+  if (st != ATTN_OK) return st;
+  if (c->B == 0 || c->T == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+  const size_t need = fwd_ws(c);
+  if (need > 0 && (!ws || ws_bytes < need)) return ATTN_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t elt = c->dtype == ATTN_BF16 ? 2 : 4;
+  const void* qh = q;
+  const void* kh = k;
+  if (c->rope || c->qk_norm) {
+    char* w = (char*)ws;
+    void* qw = w;
+    void* kw = w + align_up((size_t)c->B * c->Hq * c->T * c->D * elt);
+    hipError_t e = launch_prologue(q, qw, (int64_t)c->B * c->Hq * c->T, c->T, c->D, (int)elt,
+                                   c->rope, c->rope_base, c->qk_norm, c->norm_eps, s);
+    if (e == hipSuccess)
+      e = launch_prologue(k, kw, (int64_t)c->B * c->Hkv * c->T, c->T, c->D, (int)elt, c->rope,
+                          c->rope_base, c->qk_norm, c->norm_eps, s);
+    if (e != hipSuccess) return ATTN_ELAUNCH;
+    qh = qw;
+    kh = kw;
+  }
+  FwdParams p{qh, kh, v, o, lse, c->B, c->T, c->Hq, c->Hkv, c->D, c->window,
+              eff_scale(c->scale, c->D), c->softcap};
+  return launch_status(c->dtype == ATTN_BF16 ? launch_fwd_bf16(p, s) : launch_fwd_f32(p, s));
+}
+
+int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, const void* o,
+             const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
+             size_t ws_bytes, void* stream) {
+  int st = check_cfg(c, 1);
+  if (st != ATTN_OK) return st;
+  if (c->B == 0 || c->T == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_EINVAL;
+  const size_t need = bwd_ws(c);
+  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t qrows = (int64_t)c->B * c->Hq * c->T, krows = (int64_t)c->B * c->Hkv * c->T;
+  char* w = (char*)ws;
+  float* Dvec = (float*)w;
+  w += align_up((size_t)qrows * 4);
+  const bool pro = c->rope || c->qk_norm;
+  const void* qh = q;
+  const void* kh = k;
+  float* dqh = nullptr;
+  float* dkh = nullptr;
+  hipError_t e = hipSuccess;
+  if (pro) {
+    void* qw = w;
+    w += align_up((size_t)qrows * c->D * 2);
+    void* kw = w;
+    w += align_up((size_t)krows * c->D * 2);
+    dqh = (float*)w;
+    w += align_up((size_t)qrows * c->D * 4);
+    dkh = (float*)w;
+    e = launch_prologue(q, qw, qrows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
+                        c->norm_eps, s);
+    if (e == hipSuccess)
+      e = launch_prologue(k, kw, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
+                          c->norm_eps, s);
+    qh = qw;
+    kh = kw;
+  }
+  if (e == hipSuccess) e = launch_rowdot(dO, o, Dvec, qrows, c->D, s);
+  BwdParams p{qh, kh, v, dO, lse, Dvec, pro ? (void*)dqh : dq, pro ? (void*)dkh : dk, dv,
+              pro ? 1 : 0, c->B, c->T, c->Hq, c->Hkv, c->D, c->window,
+              eff_scale(c->scale, c->D), c->softcap};
+  if (e == hipSuccess) e = launch_bwd_dq(p, s);
+  if (e == hipSuccess) e = launch_bwd_dkdv(p, s);
+  if (pro && e == hipSuccess)
+    e = launch_epilogue(dqh, q, dq, qrows, c->T, c->D, c->rope, c->rope_base, c->qk_norm,
+                        c->norm_eps, s);
+  if (pro && e == hipSuccess)
+    e = launch_epilogue(dkh, k, dk, krows, c->T, c->D, c->rope, c->rope_base, c->qk_norm,
+                        c->norm_eps, s);
+  return launch_status(e);
+}
+
+int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* cache_len, void* o, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dcfg(c);
+  if (st != ATTN_OK) return st;
+  if (c->B == 0) return ATTN_OK;
+  if (!q || !o || !cache_len) return ATTN_EINVAL;
+  if (c->Lmax > 0 && (!k_cache || !v_cache)) return ATTN_EINVAL;
+  const size_t need = dec_ws(c);
+  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  DecodeParams p{q, k_cache, v_cache, cache_len, o, (float*)ws, c->B, c->Hq, c->Hkv, c->D,
+                 c->Lmax, decode_split_len(c), decode_nsplit(c), eff_scale(c->scale, c->D),
+                 c->softcap, c->rope, c->rope_base, c->qk_norm, c->norm_eps};
+  return launch_status(launch_decode(p, (hipStream_t)stream));
+}
+
+int attn_trace_enable(int on) {
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (on) trace_clear_locked(t);
+  t.on = on != 0;
+  return ATTN_OK;
+}
+
+int attn_trace_read(attn_trace_entry* out, int max_entries) {
+  if (max_entries < 0 || (max_entries > 0 && !out)) return ATTN_EINVAL;
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  std::vector<attn_trace_entry> agg;
+  for (auto& r : t.recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return ATTN_ELAUNCH;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return ATTN_ELAUNCH;
+    attn_trace_entry* e = nullptr;
+    for (auto& x : agg)
+      if (strncmp(x.name, r.name, sizeof(x.name)) == 0) e = &x;
+    if (!e) {
+      attn_trace_entry n;
+      memset(&n, 0, sizeof(n));
+      strncpy(n.name, r.name, sizeof(n.name) - 1);
+      agg.push_back(n);
+      e = &agg.back();
+    }
+    e->launches += 1;
+    e->total_ms += ms;
+  }
+  const int n = (int)agg.size();
+  for (int i = 0; i < n && i < max_entries; ++i) out[i] = agg[i];
+  return n;
+}
+
+}  // extern "C"

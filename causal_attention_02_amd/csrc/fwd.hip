@@ -1,0 +1,379 @@
+// Causal attention forward on gfx950.
+//
+// Definition ("GPT pretraining" page, section "Multihead Attention"):
+//   O = softmax(S) V with S = scale * Q K^T, future positions set to -inf before the
+//   softmax; optional soft-cap S <- c tanh(S / c) and sliding window (flaxchat page,
+//   "Core Features"; nanoGPT-JAX 181M model card, "Architecture").
+// The result is reached exactly (up to rounding) by the flash formulation: key tiles are
+// visited once, a running row maximum m and row sum l rescale the partial output, and
+// LSE = m + ln(l) is kept for the backward.
+//
+// bf16 kernel layout (one workgroup = (b, h, 128 queries), 4 waves x 32 queries):
+//   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that a lane holds 16
+//     scores of ONE query (lane % 32) per 32-key block: the row max / sum is a per-lane
+//     reduction plus one permlane32 swap with the partner lane l ^ 32.
+//   * Q stays in registers as the MFMA B operand for the whole kernel.
+//   * K and V tiles (64 keys) are staged row-major in LDS, double buffered.  K feeds the
+//     A operand directly; V^T is read with ds_read_b64_tr_b16, and P goes from the score
+//     accumulators straight into the B operand of O^T += V^T P^T (no LDS round trip).
+//   * Key tiles wholly above the diagonal or outside the window are never visited; only
+//     tiles that straddle a mask edge evaluate the element mask.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+
+namespace {
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int B, T, Hq, Hkv, window, nqt;
+  float scale_log2;  // scale * log2(e)
+  float cap_k1;      // 2 * scale * log2(e) / c : tanh(x) = 1 - 2 / (2^(S * cap_k1) + 1)
+  float cap_k2;      // c * log2(e)
+};
+
+constexpr int kBM = 128;  // queries per workgroup
+constexpr int kBN = 64;   // keys per tile
+
+template <int D, bool CAP>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int LD = D + 8;          // LDS row pitch (elements)
+  constexpr int NS = D / 16;         // MFMA k-steps over the head dimension
+  constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int CPT = kBN * CPR / 256;  // chunks per thread per tile
+  static_assert(kBN * CPR % 256 == 0, "tile must split evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][kBN * LD];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][kBN * LD];
+
+  const int T = a.T;
+  const int nbh = a.B * a.Hq;
+  const int rank = blockIdx.x / nbh;  // heaviest (last) query tiles first
+  const int bh = blockIdx.x - rank * nbh;
+  const int qt = a.nqt - 1 - rank;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int g = h / (a.Hq / a.Hkv);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int q0 = qt * kBM, qw0 = q0 + 32 * w;
+  const int qi = qw0 + lr;
+  const int window = a.window;
+
+  const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * T * D;
+  const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
+
+  // Q operand: lane holds Q[qi][16 s + 8 gl .. +7].
+  bf16x8 bq[NS];
+  {
+    const bf16* qp = a.q + ((int64_t)bh * T + min(qi, T - 1)) * D + 8 * gl;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) bq[s] = ld16<bf16x8>(qp + 16 * s);
+  }
+
+  const int k_end = min(T, q0 + kBM);
+  const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
+  const int kt0 = k_begin / kBN, kt1 = (k_end - 1) / kBN;
+
+  uint4 rk[CPT], rv[CPT];
+  auto gload = [&](int kt) {
+    const int k0 = kt * kBN;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + 256 * c;
+      const int row = idx / CPR, col = (idx - row * CPR) * 8;
+      const int key = k0 + row;
+      if (key < T) {
+        rk[c] = ld16<uint4>(kbase + (int64_t)key * D + col);
+        rv[c] = ld16<uint4>(vbase + (int64_t)key * D + col);
+      } else {
+        rk[c] = make_uint4(0, 0, 0, 0);
+        rv[c] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + 256 * c;
+      const int row = idx / CPR, col = (idx - row * CPR) * 8;
+      *reinterpret_cast<uint4*>(&sK[buf][row * LD + col]) = rk[c];
+      *reinterpret_cast<uint4*>(&sV[buf][row * LD + col]) = rv[c];
+    }
+  };
+
+  float m_run = kNegBig, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  const bool wave_active = qw0 < T;
+  const int qw_last = min(qw0 + 31, T - 1);
+
+  gload(kt0);
+  sstore(0);
+  __syncthreads();
+  int cur = 0;
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const bool has_next = kt < kt1;
+    if (has_next) gload(kt + 1);
+    const int k0 = kt * kBN;
+    const bool skip = !wave_active || k0 > qw_last ||
+                      (window > 0 && k0 + kBN - 1 < qw0 - window + 1);
+    if (!skip) {
+      const bool need_mask = (k0 + kBN - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
+      const bf16* sk = sK[cur];
+      const bf16* sv = sV[cur];
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          sacc[kb] = mfma32(ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl), bq[s],
+                            sacc[kb]);
+      }
+      float mx = kNegBig;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[kb][r];
+          float y;
+          if constexpr (CAP) {
+            const float e = exp2_fast(x * a.cap_k1);
+            y = a.cap_k2 * (1.f - 2.f * rcp_fast(e + 1.f));
+          } else {
+            y = x * a.scale_log2;
+          }
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
+            if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
+          }
+          sacc[kb][r] = y;
+          mx = fmaxf(mx, y);
+        }
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(sacc[kb][r] - m_new);
+          sacc[kb][r] = p;
+          ls += p;
+        }
+      l_run = l_run * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        pb[kb][0] = pack8(sacc[kb], 0);
+        pb[kb][1] = pack8(sacc[kb], 8);
+      }
+      // O^T[d][q] += V^T[d][key] P^T[key][q]; lane L of each 16-lane group reads 4 values of
+      // key row (k0 + L / 4) at columns 4 (L % 4) of its 16-column half.
+      const int trow = 4 * gl + ((l & 15) >> 2);
+      const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const bf16* p0 = sv + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
+            oacc[db] = mfma32(tr_read_pair(p0, p0 + 8 * LD), pb[kb][t], oacc[db]);
+          }
+    }
+    if (has_next) sstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  const float l_tot = pair_sum(l_run);
+  if (qi < T) {
+    const float inv = 1.f / l_tot;
+    bf16* op = a.o + ((int64_t)bh * T + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] = to_bf16(oacc[db][4 * i4 + j] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i4 + 4 * gl) = v4;
+      }
+    if (gl == 0) a.lse[(int64_t)bh * T + qi] = (m_run + log2_fast(l_tot)) * kLn2;
+  }
+}
+
+// ---- fp32 forward: one thread per query, exact two-pass softmax in fp32 -----------------
+struct FwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int B, T, Hq, Hkv, window, nqt;
+  float scale, softcap;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
+  constexpr int BK = 32;
+  __shared__ float sK[BK][D];
+  __shared__ float sV[BK][D];
+  const int T = a.T;
+  const int nbh = a.B * a.Hq;
+  const int rank = blockIdx.x / nbh;
+  const int bh = blockIdx.x - rank * nbh;
+  const int qt = a.nqt - 1 - rank;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int g = h / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x;
+  const int q0 = qt * 64, qi = q0 + tid;
+  const int window = a.window;
+  const float* kb = a.k + (int64_t)(b * a.Hkv + g) * T * D;
+  const float* vb = a.v + (int64_t)(b * a.Hkv + g) * T * D;
+  float qv[D];
+  {
+    const float* qp = a.q + ((int64_t)bh * T + min(qi, T - 1)) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) qv[d] = qp[d];
+  }
+  const int k_end = min(T, q0 + 64);
+  const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
+  auto visible = [&](int key) { return key <= qi && (window <= 0 || qi - key < window); };
+  auto score = [&](int j) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(qv[d], sK[j][d], s);
+    s *= a.scale;
+    if (a.softcap > 0.f) s = a.softcap * tanhf(s / a.softcap);
+    return s;
+  };
+  float m = -INFINITY;
+  for (int k0 = (k_begin / BK) * BK; k0 < k_end; k0 += BK) {
+    for (int e = tid; e < BK * D; e += 64) {
+      const int key = k0 + e / D;
+      sK[e / D][e % D] = key < T ? kb[(int64_t)k0 * D + e] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < BK; ++j)
+      if (visible(k0 + j)) m = fmaxf(m, score(j));
+    __syncthreads();
+  }
+  float lsum = 0.f;
+  float ov[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) ov[d] = 0.f;
+  for (int k0 = (k_begin / BK) * BK; k0 < k_end; k0 += BK) {
+    for (int e = tid; e < BK * D; e += 64) {
+      const int key = k0 + e / D;
+      sK[e / D][e % D] = key < T ? kb[(int64_t)k0 * D + e] : 0.f;
+      sV[e / D][e % D] = key < T ? vb[(int64_t)k0 * D + e] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < BK; ++j)
+      if (visible(k0 + j)) {
+        const float p = expf(score(j) - m);
+        lsum += p;
+#pragma unroll
+        for (int d = 0; d < D; ++d) ov[d] = fmaf(p, sV[j][d], ov[d]);
+      }
+    __syncthreads();
+  }
+  if (qi < T) {
+    float* op = a.o + ((int64_t)bh * T + qi) * D;
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int d = 0; d < D; ++d) op[d] = ov[d] * inv;
+    a.lse[(int64_t)bh * T + qi] = m + logf(lsum);
+  }
+}
+
+template <int D>
+hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
+  FwdArgs a;
+  a.q = (const bf16*)p.q;
+  a.k = (const bf16*)p.k;
+  a.v = (const bf16*)p.v;
+  a.o = (bf16*)p.o;
+  a.lse = p.lse;
+  a.B = p.B;
+  a.T = p.T;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.window = p.window;
+  a.nqt = (p.T + kBM - 1) / kBM;
+  a.scale_log2 = p.scale * kLog2e;
+  const bool cap = p.softcap > 0.f;
+  a.cap_k1 = cap ? 2.f * p.scale * kLog2e / p.softcap : 0.f;
+  a.cap_k2 = cap ? p.softcap * kLog2e : 0.f;
+  const dim3 grid((unsigned)(a.nqt * p.B * p.Hq));
+  static const char* names[4] = {"fwd_bf16_d32", "fwd_bf16_d64", "fwd_bf16_d96", "fwd_bf16_d128"};
+  TraceScope t(names[D / 32 - 1], s);
+  if (cap)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_f32_d(const FwdParams& p, hipStream_t s) {
+  FwdF32Args a;
+  a.q = (const float*)p.q;
+  a.k = (const float*)p.k;
+  a.v = (const float*)p.v;
+  a.o = (float*)p.o;
+  a.lse = p.lse;
+  a.B = p.B;
+  a.T = p.T;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.window = p.window;
+  a.nqt = (p.T + 63) / 64;
+  a.scale = p.scale;
+  a.softcap = p.softcap;
+  TraceScope t("fwd_f32", s);
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)(a.nqt * p.B * p.Hq)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_fwd_bf16_d<32>(p, s);
+    case 64: return launch_fwd_bf16_d<64>(p, s);
+    case 96: return launch_fwd_bf16_d<96>(p, s);
+    case 128: return launch_fwd_bf16_d<128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_fwd_f32_d<32>(p, s);
+    case 64: return launch_fwd_f32_d<64>(p, s);
+    case 96: return launch_fwd_f32_d<96>(p, s);
+    case 128: return launch_fwd_f32_d<128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

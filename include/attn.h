@@ -1,0 +1,160 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) causal self-attention library (libcausal_attn.so).
+ *
+ * What is computed.  For every batch b and query head h (KV head g = h / (Hq / Hkv),
+ * contiguous groups -- grouped-query attention as on the nanoGPT-JAX 181M model card,
+ * "Architecture": 8 query heads over 4 KV heads):
+ *
+ *     q^ = N(R(q)),  k^ = N(R(k))                     (prologue, each optional)
+ *     S  = scale * q^ k^T                             (scale = 1/sqrt(D) by default)
+ *     S  = c * tanh(S / c)                            (logit soft-cap, optional)
+ *     S_ij = -inf unless j <= i and (W == 0 or i - j < W)
+ *     O  = softmax_rows(S) V,   LSE_i = ln sum_j exp(S_ij)
+ *
+ * The definition softmax(Q K^T / sqrt(d_k)) V and the causal rule (future scores set to
+ * -inf before the softmax) are those of the "GPT pretraining" page (llm_gpt_pretrain),
+ * section "Multihead Attention"; heads are laid out [B, H, T, D] as that page's
+ * _split_heads produces.  R is RoPE (pairs (x_i, x_{i+D/2}) rotated by p * base^(-2i/D)),
+ * N the parameter-free RMSNorm x / sqrt(mean(x^2) + eps) -- both named on the nanoGPT-JAX
+ * 181M model card ("Design choices worth naming") and on the flaxchat page ("Core
+ * Features"), which also names the sliding window.  The KV-cache decode follows the
+ * "Bonus: KV Caching" section of the GPT pretraining page: the new token's key/value are
+ * already in the cache and its single query attends over the whole cached history.
+ *
+ * Conventions for every entry point below.
+ *  - Pointers marked "device" are device memory owned by the caller; the library never
+ *    allocates, frees or keeps them.  Tensors are dense and row-major in the stated shape.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  No call
+ *    synchronises the host.  Calls share no mutable state and may run concurrently on
+ *    different streams with different buffers.
+ *  - Argument errors are reported by a negative status BEFORE anything is enqueued.
+ *    A failed launch is reported as ATTN_ELAUNCH.  Faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - One element type (cfg->dtype) is used for q, k, v, o, dO, dq, dk, dv; LSE is always
+ *    float32 natural-log, shape [B, Hq, T].
+ */
+#ifndef CAUSAL_ATTN_H
+#define CAUSAL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,       /* a null pointer, a negative or inconsistent size, Hq % Hkv != 0 ... */
+  ATTN_EUNSUPPORTED = -2, /* valid but not implemented: D not in {32,64,96,128}, fp32 backward ... */
+  ATTN_EWORKSPACE = -3,   /* workspace missing or smaller than the *_workspace_bytes() figure   */
+  ATTN_ELAUNCH = -4       /* the HIP runtime refused a launch                                   */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Training forward/backward configuration. */
+typedef struct {
+  int32_t B, T;        /* batch, sequence length (>= 0; 0 means nothing to do)                 */
+  int32_t Hq, Hkv;     /* query heads, KV heads; Hq % Hkv == 0                                  */
+  int32_t D;           /* head dimension: 32, 64, 96 or 128                                     */
+  int32_t window;      /* 0 = plain causal; W > 0: key j visible to query i iff i - W < j <= i  */
+  float softcap;       /* 0 = off; c > 0: S <- c * tanh(S / c) on the scaled scores             */
+  float scale;         /* 0 = 1/sqrt(D)                                                         */
+  int32_t rope;        /* 1 = rotate q and k rows at positions 0..T-1                           */
+  float rope_base;     /* RoPE base (10000 on the pages' models); > 0 when rope = 1             */
+  int32_t qk_norm;     /* 1 = parameter-free RMSNorm of every q and k row (after RoPE)          */
+  float norm_eps;      /* RMSNorm epsilon (> 0 when qk_norm = 1)                                */
+  int32_t dtype;       /* attn_dtype: ATTN_BF16 for everything, ATTN_F32 for the forward only   */
+} attn_cfg;
+
+/* Single-token KV-cache decode configuration (bfloat16 only). */
+typedef struct {
+  int32_t B;           /* sequences (>= 0)                                                      */
+  int32_t Hq, Hkv, D;  /* as in attn_cfg                                                        */
+  int32_t Lmax;        /* allocated cache rows per (b, kv head), >= 0                           */
+  float softcap;       /* as in attn_cfg                                                        */
+  float scale;         /* 0 = 1/sqrt(D)                                                         */
+  int32_t rope;        /* 1 = rotate the query at position cache_len[b] - 1                    */
+  float rope_base;
+  int32_t qk_norm;     /* 1 = RMSNorm the query (cached keys are stored already normalised)     */
+  float norm_eps;
+  int32_t split_len;   /* keys per split-K chunk: 0 = library default, else a multiple of 64    */
+} attn_decode_cfg;
+
+/* Bytes of device workspace that attn_fwd / attn_bwd / attn_decode need for this
+ * configuration (0 if none).  Host-only; returns 0 for an invalid configuration. */
+size_t attn_fwd_workspace_bytes(const attn_cfg* cfg);
+size_t attn_bwd_workspace_bytes(const attn_cfg* cfg);
+size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg);
+
+/* Host-only validation of a configuration; the status attn_fwd would return for it
+ * (before pointer and workspace checks).  for_backward = 1 applies the backward's rules. */
+int attn_check_cfg(const attn_cfg* cfg, int for_backward);
+int attn_check_decode_cfg(const attn_decode_cfg* cfg);
+
+/*
+ * attn_fwd -- flash-style forward.
+ *   q   [B, Hq,  T, D] device, dtype      k, v [B, Hkv, T, D] device, dtype
+ *   o   [B, Hq,  T, D] device, dtype (written)
+ *   lse [B, Hq,  T]    device, float32 natural-log log-sum-exp of each score row (written);
+ *                      the backward consumes it.
+ *   ws  device workspace of ws_bytes >= attn_fwd_workspace_bytes(cfg) (may be NULL if 0).
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_fwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, void* o,
+             float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * attn_bwd -- gradients of sum(O * dO) with respect to the RAW q, k, v (before RoPE and
+ * QK-norm).  bfloat16 only.  q, k, v, o, lse are exactly what attn_fwd consumed/produced.
+ *   dO [B, Hq, T, D] device, bf16;  dq [B, Hq, T, D], dk, dv [B, Hkv, T, D] device, bf16
+ *   (written; dk/dv hold the sums over each KV head's query group).
+ *   ws device workspace of ws_bytes >= attn_bwd_workspace_bytes(cfg).
+ * The result is deterministic (no atomics).
+ */
+int attn_bwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, const void* o,
+             const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
+             size_t ws_bytes, void* stream);
+
+/*
+ * attn_decode -- one new query per sequence against its KV cache (split-K over the cache
+ * length, then an LSE-weighted merge of the chunks).  bfloat16 only.
+ *   q         [B, Hq, D] device, bf16 -- raw (un-rotated) query of the newest token
+ *   k_cache   [B, Hkv, Lmax, D] device, bf16 -- keys already rotated (and normalised when
+ *             qk_norm = 1); the newest token's key is already appended
+ *   v_cache   [B, Hkv, Lmax, D] device, bf16
+ *   cache_len [B] device, int32 -- active rows L_b; only rows 0..L_b-1 are read.  Values
+ *             are clamped to [0, Lmax] in the kernel; L_b = 0 yields a zero output row.
+ *   o         [B, Hq, D] device, bf16 (written)
+ *   ws        device workspace of ws_bytes >= attn_decode_workspace_bytes(cfg).
+ */
+int attn_decode(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* cache_len, void* o, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_str(int status);
+
+/*
+ * Kernel tracing (a measurement aid, off by default).  While enabled, every kernel the
+ * library enqueues is bracketed by a pair of HIP events on its stream; attn_trace_read
+ * synchronises those events and reports, per kernel name, the number of launches and
+ * their summed device time.  The trace is process-wide state: enable/read/disable from
+ * one thread while no other thread calls the library.
+ */
+typedef struct {
+  char name[48];       /* kernel family, e.g. "fwd_bf16_d128"                                   */
+  int64_t launches;    /* launches recorded since the last reset                                */
+  double total_ms;     /* summed event-to-event time of those launches                          */
+} attn_trace_entry;
+
+int attn_trace_enable(int on);                       /* on = 1 starts (and clears), 0 stops    */
+int attn_trace_read(attn_trace_entry* out, int max_entries);  /* returns the entry count (>= 0)
+                                                                 or a negative attn_status     */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_ATTN_H */

@@ -1,0 +1,124 @@
+"""The C ABI library loads, exports every symbol include/attn.h declares, and rejects bad
+arguments on the host before anything is enqueued.  No GPU is needed: every call here
+either touches no HIP API at all or returns before the first one."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_attention_02_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(bd.EXPORTED) == names
+
+
+def cfg(**kw):
+    base = dict(B=2, T=128, Hq=8, Hkv=4, D=96, opts=bd.AttnOptions(softcap=50.0, rope=True,
+                                                                     qk_norm=True),
+                dtype=bd.ATTN_BF16)
+    base.update(kw)
+    return bd.make_cfg(base["B"], base["T"], base["Hq"], base["Hkv"], base["D"], base["opts"],
+                       base["dtype"])
+
+
+def test_config_validation(L):
+    ok = cfg()
+    assert L.attn_check_cfg(ctypes.byref(ok), 0) == bd.ATTN_OK
+    assert L.attn_check_cfg(ctypes.byref(ok), 1) == bd.ATTN_OK
+    assert L.attn_check_cfg(None, 0) == bd.ATTN_EINVAL
+    bad = [cfg(Hq=6, Hkv=4), cfg(B=-1), cfg(T=-3), cfg(Hkv=0),
+           cfg(opts=bd.AttnOptions(window=-1)), cfg(opts=bd.AttnOptions(softcap=-1.0)),
+           cfg(opts=bd.AttnOptions(softcap=float("nan"))), cfg(opts=bd.AttnOptions(scale=float("inf"))),
+           cfg(opts=bd.AttnOptions(rope=True, rope_base=0.0)),
+           cfg(opts=bd.AttnOptions(qk_norm=True, norm_eps=0.0)), cfg(dtype=7), cfg(D=0)]
+    for c in bad:
+        assert L.attn_check_cfg(ctypes.byref(c), 0) == bd.ATTN_EINVAL
+    for D in (16, 48, 80, 256):
+        assert L.attn_check_cfg(ctypes.byref(cfg(D=D)), 0) == bd.ATTN_EUNSUPPORTED
+    f32 = cfg(dtype=bd.ATTN_F32)
+    assert L.attn_check_cfg(ctypes.byref(f32), 0) == bd.ATTN_OK
+    assert L.attn_check_cfg(ctypes.byref(f32), 1) == bd.ATTN_EUNSUPPORTED
+
+
+def test_workspace_sizes(L):
+    c = cfg(B=16, T=2048)
+    rows = 16 * 8 * 2048
+    q_elems, k_elems = rows * 96, 16 * 4 * 2048 * 96
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(c)) == q_elems * 2 + k_elems * 2
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(c)) == rows * 4 + (q_elems + k_elems) * 6
+    plain = cfg(B=16, T=2048, opts=bd.AttnOptions())
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(plain)) == 0
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == rows * 4
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(Hq=5))) == 0  # invalid -> 0
+    d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(softcap=50.0, rope=True))
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 8 * 98 * 4
+    d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(), split_len=128)
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 16 * 98 * 4
+
+
+def test_decode_config_validation(L):
+    o = bd.AttnOptions(softcap=50.0, rope=True)
+    assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, 2048, o))) == 0
+    assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 3, 96, 2048, o))) == -1
+    assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, -1, o))) == -1
+    assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, 2048, o, 100))) == -1
+    assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 80, 2048, o))) == -2
+
+
+def test_entry_points_reject_before_launch(L):
+    """Invalid configs, null pointers and short workspaces return an error status without
+    any HIP call (this process has no GPU, so reaching one would fail differently)."""
+    c = cfg()
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    s = ctypes.c_void_p(0)
+    bad = cfg(Hq=6, Hkv=4)
+    assert L.attn_fwd(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, 1 << 40, s) == -1
+    assert L.attn_fwd(ctypes.byref(c), null, fake, fake, fake, fake, fake, 1 << 40, s) == -1
+    assert L.attn_fwd(ctypes.byref(c), fake, fake, fake, fake, fake, null, 0, s) == -3
+    assert L.attn_fwd(ctypes.byref(c), fake, fake, fake, fake, fake, fake, 16, s) == -3
+    assert L.attn_bwd(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                      16, s) == -3
+    assert L.attn_bwd(ctypes.byref(c), fake, fake, fake, fake, null, fake, fake, fake, fake, fake,
+                      1 << 40, s) == -1
+    f32 = cfg(dtype=bd.ATTN_F32)
+    assert L.attn_bwd(ctypes.byref(f32), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                      1 << 40, s) == -2
+    d = bd.make_decode_cfg(4, 8, 4, 96, 64, bd.AttnOptions())
+    assert L.attn_decode(ctypes.byref(d), fake, fake, fake, fake, fake, null, 0, s) == -3
+    assert L.attn_decode(ctypes.byref(d), fake, fake, fake, null, fake, fake, 1 << 40, s) == -1
+    # Empty problems are valid and enqueue nothing.
+    assert L.attn_fwd(ctypes.byref(cfg(T=0)), null, null, null, null, null, null, 0, s) == 0
+    assert L.attn_bwd(ctypes.byref(cfg(B=0)), null, null, null, null, null, null, null, null, null,
+                      null, 0, s) == 0
+    d0 = bd.make_decode_cfg(0, 8, 4, 96, 64, bd.AttnOptions())
+    assert L.attn_decode(ctypes.byref(d0), null, null, null, null, null, null, 0, s) == 0
+
+
+def test_status_strings_and_trace(L):
+    assert bd.status_str(0) == "ok"
+    assert "workspace" in bd.status_str(-3)
+    assert bd.status_str(12345) == "unknown status"
+    bd.trace_enable(True)
+    assert bd.trace_read() == {}
+    bd.trace_enable(False)

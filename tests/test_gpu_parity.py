@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on seeded inputs.
+
+Small cases compare every element; the full-size workloads (the shapes bench.py times, in
+the same launch configuration) compare sampled (batch, KV-group) slices, each of which the
+oracle computes exactly.  Tolerances: fp32 forward max-abs 1e-5; bf16 relative L2 1e-2
+on O and 2e-2 on dQ/dK/dV; LSE absolute 2e-2 (bf16 inputs).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from causal_attention_02_amd import AttnOptions, attn_bwd, attn_decode, attn_fwd
+from causal_attention_02_amd.inputs import WORKLOADS, Workload, make_decode_inputs, make_train_inputs
+from oracle import attention_backward, attention_decode, attention_forward, rms_normalize, rope_rotate
+from tests.util import (TOL_F32_MAXABS, TOL_GRAD, TOL_LSE_BF16, TOL_O, max_abs, rel_l2, to_dev,
+                        to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def opts_of(w: Workload) -> AttnOptions:
+    return AttnOptions(window=w.window, softcap=w.softcap, rope=w.rope, rope_base=w.rope_base,
+                       qk_norm=w.qk_norm, norm_eps=w.norm_eps)
+
+
+def oracle_kw(w: Workload) -> dict:
+    return dict(window=w.window, softcap=w.softcap, rope=w.rope, rope_base=w.rope_base,
+                qk_norm=w.qk_norm, norm_eps=w.norm_eps)
+
+
+def gpu_fwd_bwd(w: Workload, q, k, v, dO):
+    import torch
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    tq, tk, tv = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    o, lse = attn_fwd(tq, tk, tv, opts_of(w))
+    grads = None
+    if dO is not None:
+        tdo = to_dev(dO, dt)
+        grads = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))
+    torch.cuda.synchronize()
+    out = (to_host(o), to_host(lse))
+    if grads is not None:
+        out = out + tuple(to_host(g) for g in grads)
+    return out
+
+
+def check_bf16(w, got, ref_fwd, ref_bwd, tag, tol_grad=TOL_GRAD):
+    O, L = got[0], got[1]
+    eO, eL = rel_l2(O, ref_fwd[0]), max_abs(L, ref_fwd[1])
+    msg = f"{tag}: relL2(O)={eO:.2e} maxabs(LSE)={eL:.2e}"
+    assert np.isfinite(O).all() and np.isfinite(L).all(), tag
+    assert eO <= TOL_O, msg
+    assert eL <= TOL_LSE_BF16, msg
+    if ref_bwd is not None:
+        errs = [rel_l2(g, r) for g, r in zip(got[2:], ref_bwd)]
+        msg += " relL2(dQ,dK,dV)=" + ",".join(f"{e:.2e}" for e in errs)
+        for g in got[2:]:
+            assert np.isfinite(g).all(), tag
+        assert max(errs) <= tol_grad, msg
+    _say(msg)
+
+
+# --------------------------------------------------------------------------------------------
+# fp32 forward (MiniGPT shape, full size)
+# --------------------------------------------------------------------------------------------
+def test_minigpt_fp32_forward_full():
+    w = WORKLOADS["minigpt_fwd_f32"]
+    _say(f"case {w.name} seed {w.seed}")
+    q, k, v, _ = make_train_inputs(w)
+    O, L = gpu_fwd_bwd(w, q, k, v, None)
+    Or, Lr = attention_forward(q, k, v, **oracle_kw(w))
+    assert max_abs(O, Or) <= TOL_F32_MAXABS, max_abs(O, Or)
+    assert max_abs(L, Lr) <= TOL_F32_MAXABS, max_abs(L, Lr)
+
+
+@pytest.mark.parametrize("D,T,flags", [(64, 77, dict(window=9, softcap=3.0)),
+                                       (96, 130, dict(rope=True, qk_norm=True, softcap=50.0)),
+                                       (128, 65, dict(rope=True)), (32, 1, {})])
+def test_fp32_forward_variants(D, T, flags):
+    w = Workload("f32var", B=2, T=T, Hq=4, Hkv=2, D=D, dtype="f32", backward=False, seed=5, **flags)
+    _say(f"case f32 D={D} T={T} {flags}")
+    q, k, v, _ = make_train_inputs(w)
+    O, L = gpu_fwd_bwd(w, q, k, v, None)
+    Or, Lr = attention_forward(q, k, v, **oracle_kw(w))
+    assert max_abs(O, Or) <= TOL_F32_MAXABS
+    assert max_abs(L, Lr) <= TOL_F32_MAXABS
+
+
+# --------------------------------------------------------------------------------------------
+# bf16 forward + backward, whole tensors against the oracle
+# --------------------------------------------------------------------------------------------
+SMALL = [
+    WORKLOADS["minigpt_train_bf16"],  # full size: 32 x 6 heads x 128 x 32
+    WORKLOADS["gqa181m_train"].with_(name="gqa181m_small", B=2, T=300),
+    WORKLOADS["flaxchat_full"].with_(name="flaxchat_small", B=1, T=333),
+    WORKLOADS["flaxchat_w512"].with_(name="flaxchat_w512_small", B=1, T=700),
+    WORKLOADS["flaxchat_w512"].with_(name="window100", B=2, T=333, window=100, D=64, Hq=4, Hkv=2),
+    Workload("tiny_T1", B=3, T=1, Hq=2, Hkv=1, D=32, rope=True, qk_norm=True, softcap=5.0),
+    Workload("tiny_T2", B=1, T=2, Hq=2, Hkv=2, D=64),
+    Workload("ragged65", B=2, T=65, Hq=3, Hkv=1, D=128, softcap=0.5),
+    Workload("ragged129", B=1, T=129, Hq=2, Hkv=1, D=96, rope=True),
+    Workload("window1", B=1, T=70, Hq=2, Hkv=1, D=32, window=1, rope=True, qk_norm=True),
+    Workload("window_gt_T", B=1, T=200, Hq=2, Hkv=2, D=64, window=205, qk_norm=True),
+    Workload("mha_d64", B=2, T=256, Hq=4, Hkv=4, D=64, rope=True, softcap=20.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_bf16_fwd_bwd_small(w):
+    _say(f"case {w.name}: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} W={w.window} "
+         f"cap={w.softcap} rope={w.rope} norm={w.qk_norm}")
+    q, k, v, dO = make_train_inputs(w)
+    got = gpu_fwd_bwd(w, q, k, v, dO)
+    ref_f = attention_forward(q, k, v, **oracle_kw(w))
+    ref_b = attention_backward(q, k, v, dO, **oracle_kw(w))
+    # With T <= 2 the first row of dQ (and the last row of dK) is exactly zero; there the
+    # backward leaves the residue of D_i = dO_i . O_i taken from the bf16-rounded O, about
+    # 2^-9 |dO_i| |O_i| / sqrt(D) -- a few percent of these tiny tensors' norms.
+    check_bf16(w, got, ref_f, ref_b, w.name, tol_grad=TOL_GRAD if w.T > 2 else 5e-2)
+
+
+def test_window_one_identity_on_gpu():
+    """W = 1: O = V exactly (P is the identity), dV = dO, dQ = dK = 0."""
+    w = Workload("w1", B=1, T=130, Hq=2, Hkv=2, D=64, window=1, rope=True)
+    q, k, v, dO = make_train_inputs(w)
+    O, L, dq, dk, dv = gpu_fwd_bwd(w, q, k, v, dO)
+    assert np.array_equal(O, v)
+    assert np.array_equal(dv, dO)
+    # dS = P (dP - D) vanishes up to the rounding difference of two fp32 dot products.
+    assert np.abs(dq).max() <= 1e-3 and np.abs(dk).max() <= 1e-3
+
+
+# --------------------------------------------------------------------------------------------
+# Full-size workloads, sampled (b, kv-group) slices
+# --------------------------------------------------------------------------------------------
+FULL = ["gqa181m_train", "flaxchat_full", "flaxchat_w512"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = WORKLOADS[name]
+    _say(f"case {name} full size: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
+    q, k, v, dO = make_train_inputs(w)
+    got = gpu_fwd_bwd(w, q, k, v, dO)
+    G = w.Hq // w.Hkv
+    for b, g in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+        hs = slice(g * G, (g + 1) * G)
+        qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
+        ref_f = attention_forward(qs, ks, vs, **oracle_kw(w))
+        ref_b = attention_backward(qs, ks, vs, dos, **oracle_kw(w))
+        sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
+              got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
+        check_bf16(w, sl, ref_f, ref_b, f"{name}[b={b},g={g}]")
+
+
+def test_backward_is_deterministic():
+    import torch
+    w = WORKLOADS["gqa181m_train"].with_(B=2, T=512)
+    q, k, v, dO = make_train_inputs(w)
+    tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+    o, lse = attn_fwd(tq, tk, tv, opts_of(w))
+    g1 = [t.clone() for t in attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))]
+    g2 = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))
+    o2, lse2 = attn_fwd(tq, tk, tv, opts_of(w))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------------------------
+# Decode
+# --------------------------------------------------------------------------------------------
+def gpu_decode(w, q, kc, vc, lens, split_len=0):
+    import torch
+    o = attn_decode(to_dev(q, torch.bfloat16), to_dev(kc, torch.bfloat16),
+                    to_dev(vc, torch.bfloat16), torch.from_numpy(lens).to("cuda"),
+                    opts_of(w), split_len=split_len)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+def test_decode_full_size():
+    w = WORKLOADS["gqa181m_decode"]
+    _say(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} Lmax={w.T}")
+    q, kc, vc, lens = make_decode_inputs(w)
+    o = gpu_decode(w, q, kc, vc, lens)
+    ref = attention_decode(q, kc, vc, lens, **{k: v for k, v in oracle_kw(w).items() if k != "window"})
+    e = rel_l2(o, ref)
+    _say(f"decode relL2={e:.2e}")
+    assert e <= TOL_O
+
+
+def test_decode_reads_only_active_rows_and_split_invariance():
+    """Rows at or past cache_len are NaN: any read of them would poison the output.
+    Results agree across split sizes to fp32 rounding (then bf16 output rounding)."""
+    w = WORKLOADS["gqa181m_decode"].with_(B=9, T=640)
+    q, kc, vc, lens = make_decode_inputs(w)
+    lens = np.array([0, 1, 63, 64, 65, 300, 639, 640, 700], dtype=np.int32)
+    kc, vc = kc.copy(), vc.copy()
+    for b, L in enumerate(lens):
+        kc[b, :, max(L, 0):] = np.nan
+        vc[b, :, max(L, 0):] = np.nan
+    kw = {k: v for k, v in oracle_kw(w).items() if k != "window"}
+    ref = attention_decode(q, np.nan_to_num(kc), np.nan_to_num(vc), lens, **kw)
+    outs = []
+    for sl in (64, 128, 256, 704):
+        o = gpu_decode(w, q, kc, vc, lens, split_len=sl)
+        assert np.isfinite(o).all(), sl
+        assert np.array_equal(o[0], np.zeros_like(o[0]))
+        e = rel_l2(o, ref)
+        assert e <= TOL_O, (sl, e)
+        outs.append(o)
+    for o in outs[1:]:
+        assert rel_l2(o, outs[0]) <= 4e-3
+
+
+def test_decode_matches_last_forward_row():
+    """Decode over a cache of rotated keys equals the last row of the training forward."""
+    import torch
+    w = Workload("dec_vs_fwd", B=3, T=257, Hq=8, Hkv=4, D=96, softcap=50.0, rope=True, seed=9)
+    q, k, v, _ = make_train_inputs(w)
+    O, _ = gpu_fwd_bwd(w.with_(backward=False), q, k, v, None)
+    kc = rope_rotate(k, np.arange(w.T))
+    from causal_attention_02_amd.inputs import round_to_bf16
+    kc = round_to_bf16(kc.astype(np.float32))
+    lens = np.full(w.B, w.T, dtype=np.int32)
+    o = gpu_decode(w, q[:, :, -1], kc, v, lens)
+    assert rel_l2(o, O[:, :, -1]) <= TOL_O
+
+
+def test_decode_with_qk_norm():
+    w = Workload("dec_norm", B=5, T=300, Hq=6, Hkv=2, D=128, rope=True, qk_norm=True, decode=True,
+                 backward=False, len_lo=1, seed=3)
+    q, kc, vc, lens = make_decode_inputs(w)
+    kc = rms_normalize(kc)[0].astype(np.float32)
+    from causal_attention_02_amd.inputs import round_to_bf16
+    kc = round_to_bf16(kc)
+    o = gpu_decode(w, q, kc, vc, lens)
+    kw = {k: v for k, v in oracle_kw(w).items() if k != "window"}
+    assert rel_l2(o, attention_decode(q, kc, vc, lens, **kw)) <= TOL_O
+
+
+# --------------------------------------------------------------------------------------------
+# Error paths through the binding on a GPU (nothing is launched)
+# --------------------------------------------------------------------------------------------
+def test_errors_on_gpu():
+    import torch
+    from causal_attention_02_amd import AttnError
+    q = torch.zeros(1, 6, 8, 96, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 4, 8, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(AttnError):
+        attn_fwd(q, k, k)  # 6 query heads over 4 KV heads
+    q = torch.zeros(1, 4, 8, 80, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 4, 8, 80, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(AttnError):
+        attn_fwd(q, k, k)  # D = 80 unsupported
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        attn_fwd(q, k, k, AttnOptions(rope=True), workspace=small)
