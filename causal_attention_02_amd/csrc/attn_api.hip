@@ -116,15 +116,15 @@ int decode_nsplit(const attn_decode_cfg* c) {
   return c->Lmax > 0 ? (c->Lmax + sl - 1) / sl : 1;
 }
 
-// Workspace layouts (each region 256-byte aligned):
-//   fwd: [q^ B*Hq*T*D elt][k^ B*Hkv*T*D elt]                      when rope or qk_norm
-//   bwd: [D B*Hq*T f32] + when rope or qk_norm:
-//        [q^ bf16][k^ bf16][dq^ f32 B*Hq*T*D][dk^ f32 B*Hkv*T*D]
+// Workspace layouts (each region 256-byte aligned), when RoPE or QK-norm is on:
+//   fwd bf16: [k^ B*Hkv*T*D bf16]       (q gets its prologue inside the forward kernel)
+//   fwd f32:  [q^ B*Hq*T*D f32][k^ B*Hkv*T*D f32]
+//   bwd:      [D B*Hq*T f32][q^ bf16][k^ bf16]   (without RoPE/QK-norm only D)
 size_t fwd_ws(const attn_cfg* c) {
   if (!(c->rope || c->qk_norm)) return 0;
-  const size_t elt = c->dtype == ATTN_BF16 ? 2 : 4;
   const size_t nq = (size_t)c->B * c->Hq * c->T * c->D, nk = (size_t)c->B * c->Hkv * c->T * c->D;
-  return align_up(nq * elt) + align_up(nk * elt);
+  if (c->dtype == ATTN_BF16) return align_up(nk * 2);
+  return align_up(nq * 4) + align_up(nk * 4);
 }
 
 size_t bwd_ws(const attn_cfg* c) {
@@ -132,7 +132,7 @@ size_t bwd_ws(const attn_cfg* c) {
   size_t s = align_up(rows * 4);
   if (c->rope || c->qk_norm) {
     const size_t nq = rows * c->D, nk = (size_t)c->B * c->Hkv * c->T * c->D;
-    s += align_up(nq * 2) + align_up(nk * 2) + align_up(nq * 4) + align_up(nk * 4);
+    s += align_up(nq * 2) + align_up(nk * 2);
   }
   return s;
 }
@@ -180,25 +180,34 @@ int attn_fwd(const attn_cfg* c, const void* q, const void* k, const void* v, voi
   const size_t need = fwd_ws(c);
   if (need > 0 && (!ws || ws_bytes < need)) return ATTN_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const size_t elt = c->dtype == ATTN_BF16 ? 2 : 4;
-  const void* qh = q;
-  const void* kh = k;
-  if (c->rope || c->qk_norm) {
-    char* w = (char*)ws;
-    void* qw = w;
-    void* kw = w + align_up((size_t)c->B * c->Hq * c->T * c->D * elt);
-    hipError_t e = launch_prologue(q, qw, (int64_t)c->B * c->Hq * c->T, c->T, c->D, (int)elt,
-                                   c->rope, c->rope_base, c->qk_norm, c->norm_eps, s);
-    if (e == hipSuccess)
-      e = launch_prologue(k, kw, (int64_t)c->B * c->Hkv * c->T, c->T, c->D, (int)elt, c->rope,
-                          c->rope_base, c->qk_norm, c->norm_eps, s);
-    if (e != hipSuccess) return ATTN_ELAUNCH;
-    qh = qw;
-    kh = kw;
+  const bool pro = c->rope || c->qk_norm;
+  const int64_t qrows = (int64_t)c->B * c->Hq * c->T, krows = (int64_t)c->B * c->Hkv * c->T;
+  FwdParams p{q, k, v, o, lse, c->B, c->T, c->Hq, c->Hkv, c->D, c->window,
+              eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
+              c->norm_eps};
+  hipError_t e = hipSuccess;
+  if (c->dtype == ATTN_BF16) {
+    if (pro) {
+      e = launch_prologue(k, ws, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
+                          c->norm_eps, s);
+      p.k = ws;
+    }
+    if (e == hipSuccess) e = launch_fwd_bf16(p, s);
+  } else {
+    if (pro) {
+      char* w = (char*)ws;
+      void* kw = w + align_up((size_t)qrows * c->D * 4);
+      e = launch_prologue(q, w, qrows, c->T, c->D, 4, c->rope, c->rope_base, c->qk_norm,
+                          c->norm_eps, s);
+      if (e == hipSuccess)
+        e = launch_prologue(k, kw, krows, c->T, c->D, 4, c->rope, c->rope_base, c->qk_norm,
+                            c->norm_eps, s);
+      p.q = w;
+      p.k = kw;
+    }
+    if (e == hipSuccess) e = launch_fwd_f32(p, s);
   }
-  FwdParams p{qh, kh, v, o, lse, c->B, c->T, c->Hq, c->Hkv, c->D, c->window,
-              eff_scale(c->scale, c->D), c->softcap};
-  return launch_status(c->dtype == ATTN_BF16 ? launch_fwd_bf16(p, s) : launch_fwd_f32(p, s));
+  return launch_status(e);
 }
 
 int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, const void* o,
@@ -216,39 +225,22 @@ int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, con
   float* Dvec = (float*)w;
   w += align_up((size_t)qrows * 4);
   const bool pro = c->rope || c->qk_norm;
-  const void* qh = q;
+  void* qh = const_cast<void*>(q);
   const void* kh = k;
-  float* dqh = nullptr;
-  float* dkh = nullptr;
   hipError_t e = hipSuccess;
   if (pro) {
-    void* qw = w;
+    qh = w;
     w += align_up((size_t)qrows * c->D * 2);
     void* kw = w;
-    w += align_up((size_t)krows * c->D * 2);
-    dqh = (float*)w;
-    w += align_up((size_t)qrows * c->D * 4);
-    dkh = (float*)w;
-    e = launch_prologue(q, qw, qrows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
+    e = launch_prologue(k, kw, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
                         c->norm_eps, s);
-    if (e == hipSuccess)
-      e = launch_prologue(k, kw, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
-                          c->norm_eps, s);
-    qh = qw;
     kh = kw;
   }
-  if (e == hipSuccess) e = launch_rowdot(dO, o, Dvec, qrows, c->D, s);
-  BwdParams p{qh, kh, v, dO, lse, Dvec, pro ? (void*)dqh : dq, pro ? (void*)dkh : dk, dv,
-              pro ? 1 : 0, c->B, c->T, c->Hq, c->Hkv, c->D, c->window,
-              eff_scale(c->scale, c->D), c->softcap};
+  BwdParams p{q, k, kh, qh, v, o, dO, lse, Dvec, dq, dk, dv, c->B, c->T, c->Hq, c->Hkv, c->D,
+              c->window, eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base,
+              c->qk_norm, c->norm_eps};
   if (e == hipSuccess) e = launch_bwd_dq(p, s);
   if (e == hipSuccess) e = launch_bwd_dkdv(p, s);
-  if (pro && e == hipSuccess)
-    e = launch_epilogue(dqh, q, dq, qrows, c->T, c->D, c->rope, c->rope_base, c->qk_norm,
-                        c->norm_eps, s);
-  if (pro && e == hipSuccess)
-    e = launch_epilogue(dkh, k, dk, krows, c->T, c->D, c->rope, c->rope_base, c->qk_norm,
-                        c->norm_eps, s);
   return launch_status(e);
 }
 

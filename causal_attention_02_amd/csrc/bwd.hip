@@ -1,25 +1,29 @@
-// Causal attention backward on gfx950: gradients of sum(O * dO) with respect to q^, k^, v.
+// Causal attention backward on gfx950: gradients of sum(O * dO) with respect to the raw
+// q, k, v (before RoPE and QK-norm).
 //
 // With P = exp(S - LSE) recomputed from the forward's log-sum-exp (so no T x T matrix is
 // stored), the softmax backward is
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D) with D_i = sum_d dO_id O_id,
 //     dS_pre = dS * (1 - tanh^2(S_pre / c)) when soft-capped,
-//     dq^ = scale dS_pre k^,   dk^ = scale dS_pre^T q^.
-// (The pages differentiate the attention forward of the "GPT pretraining" page, section
-// "Multihead Attention", by autodiff inside their training step; these are the same
-// derivatives written out.)
+//     dq^ = scale dS_pre k^,   dk^ = scale dS_pre^T q^,
+// and dq^, dk^ go back through RMSNorm (dy = (dy^ - y^ mean(dy^ y^)) / r) and RoPE (rotate
+// by -angle).  (The pages differentiate the attention forward of the "GPT pretraining" page,
+// section "Multihead Attention", by autodiff inside their training step; these are the
+// same derivatives written out.)
 //
-// Two kernels, no atomics:
-//  * dkdv: one workgroup per (b, kv head, 128 keys), 4 waves x 32 keys.  K^ and V of the
-//    wave's keys live in registers as MFMA B operands; the loop runs over every query head
-//    of the GQA group and every query tile that can see the keys (causal: at or below the
-//    diagonal; window: up to key + W - 1).  Q^ and dO tiles are staged row-major in LDS;
-//    S = Q^ K^T and dP = dO V^T land with one KEY per lane (lane % 32), which is the layout
-//    dV^T += dO^T P and dK^T += Q^T dS need for their B operands, and the transposed
-//    A operands come from ds_read_b64_tr_b16.  dK and dV of a KV head are summed over its
-//    query group inside the workgroup.
-//  * dq: one workgroup per (b, h, 128 queries), the forward's layout (one QUERY per lane):
-//    S^T and dP^T are recomputed, and dQ^T += K^T dS^T.
+// Two kernels, no atomics, launched dq then dkdv:
+//  * dq: one workgroup per (b, h, 128 queries), the forward's layout (one QUERY per lane).
+//    It applies the q prologue in registers (and writes q^ for dkdv), computes D_i from
+//    the dO and O rows it holds, recomputes S^T and dP^T per key tile and accumulates
+//    dQ^T += K^T dS^T; the prologue backward runs on the accumulators before the store.
+//  * dkdv: one workgroup per (b, kv head, 128 keys), 4 waves x 32 keys.  k^ (prologue in
+//    registers) and V of the wave's keys are MFMA B operands; the loop runs over every query
+//    head of the GQA group and every query tile that can see the keys (causal: at or below
+//    the diagonal; window: up to key + W - 1).  q^ and dO tiles are staged row-major in LDS;
+//    S = q^ k^T and dP = dO V^T land with one KEY per lane (lane % 32), which is the layout
+//    dV^T += dO^T P and dK^T += q^T dS need for their B operands; the transposed A operands
+//    come from ds_read_b64_tr_b16.  dK and dV of a KV head are summed over its query group
+//    inside the workgroup.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,46 +32,59 @@ namespace attn {
 namespace {
 
 struct BwdArgs {
-  const bf16* q;
-  const bf16* k;
+  const bf16* q;    // raw q
+  const bf16* k;    // raw k
+  const bf16* kh;   // k^ (dq pass)
+  bf16* qh;         // q^ (written by dq, read by dkdv)
   const bf16* v;
+  const bf16* o;
   const bf16* dO;
   const float* lse;
-  const float* Dvec;
-  void* dq;
-  void* dk;
+  float* Dvec;
+  bf16* dq;
+  bf16* dk;
   bf16* dv;
-  int grad_f32;
   int B, T, Hq, Hkv, window, ntiles;
-  float scale, scale_log2, cap_k1, cap_k2;
+  int pro;  // RoPE or QK-norm on
+  float scale;
+  ScoreCoef sc;
+  RowPrologue rp;
 };
 
-// Scaled score in log2 units; with the cap also returns t = tanh(S_pre / c).
-template <bool CAP>
-__device__ __forceinline__ float score_log2(float x, const BwdArgs& a, float* t) {
-  if constexpr (CAP) {
-    const float e = exp2_fast(x * a.cap_k1);
-    const float th = 1.f - 2.f * rcp_fast(e + 1.f);
-    *t = th;
-    return a.cap_k2 * th;
-  } else {
-    *t = 0.f;
-    return x * a.scale_log2;
-  }
+// Store 4 consecutive values of a row (accumulator layout) as bf16.
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  bf16x4 b4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b4[j] = to_bf16(v[j]);
+  *reinterpret_cast<bf16x4*>(p) = b4;
 }
 
+// Write a gradient row held as accumulators acc[db][16] (layout: d = 32 db + 8 (r/4) + 4 gl
+// + r%4) after scaling and, when RoPE/QK-norm are on, the prologue backward against the raw
+// input row xraw (at position pos).  Must be called by all lanes; stores only if `store`.
 template <int D>
-__device__ __forceinline__ void store_grad_rowpart(void* base, int64_t row, int D_, int col,
-                                                  const float* v4, bool f32) {
-  if (f32) {
-    float* p = reinterpret_cast<float*>(base) + row * D_ + col;
-    *reinterpret_cast<f32x4*>(p) = f32x4{v4[0], v4[1], v4[2], v4[3]};
-  } else {
-    bf16* p = reinterpret_cast<bf16*>(base) + row * D_ + col;
-    bf16x4 b4;
+__device__ __forceinline__ void finish_grad_row(const f32x16 (&acc)[D / 32], float scale,
+                                                const bf16* xraw, bf16* out, int pos, int gl,
+                                                bool pro, const RowPrologue& rp, bool store) {
+  constexpr int NE = D / 8;
+  float g[NE][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b4[j] = to_bf16(v4[j]);
-    *reinterpret_cast<bf16x4*>(p) = b4;
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[e][j] = acc[e / 4][4 * (e % 4) + j] * scale;
+  if (pro) {
+    float xr[NE][4];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(xraw + 8 * e + 4 * gl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[e][j] = (float)v4[j];
+    }
+    prologue_backward_acclayout<NE>(g, xr, pos, gl, rp, D);
+  }
+  if (store) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) store4(out + 8 * e + 4 * gl, g[e]);
   }
 }
 
@@ -77,7 +94,7 @@ __device__ __forceinline__ void store_grad_rowpart(void* base, int64_t row, int 
 constexpr int kBMq = 128;  // queries per dq workgroup
 constexpr int kBNk = 64;   // keys per dq tile
 
-template <int D, bool CAP>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
@@ -99,20 +116,45 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
   const int qi = qw0 + lr;
   const int qrow = min(qi, T - 1);
   const int window = a.window;
-  const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * T * D;
+  const bf16* kbase = a.kh + (int64_t)(b * a.Hkv + g) * T * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
+  const int64_t rowoff = ((int64_t)bh * T + qrow) * D;
 
   bf16x8 bq[NS], bdo[NS];
+  float Di;
   {
-    const int64_t off = ((int64_t)bh * T + qrow) * D + 8 * gl;
+    const int64_t off = rowoff + 8 * gl;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       bq[s] = ld16<bf16x8>(a.q + off + 16 * s);
       bdo[s] = ld16<bf16x8>(a.dO + off + 16 * s);
     }
+    if (a.pro) {
+      float x[NS][8];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) x[s][p] = (float)bq[s][p];
+      prologue_oplayout<NS>(x, qrow, gl, a.rp, D);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) bq[s][p] = to_bf16(x[s][p]);
+        if (qi < T) *reinterpret_cast<bf16x8*>(a.qh + off + 16 * s) = bq[s];
+      }
+    }
+    // D_i = dO_i . O_i from the rows this lane pair holds.
+    float dsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 ov = ld16<bf16x8>(a.o + off + 16 * s);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) dsum = fmaf((float)bdo[s][p], (float)ov[p], dsum);
+    }
+    Di = pair_sum(dsum);
+    if (gl == 0 && qi < T) a.Dvec[(int64_t)bh * T + qi] = Di;
   }
   const float lse2 = a.lse[(int64_t)bh * T + qrow] * kLog2e;
-  const float Di = a.Dvec[(int64_t)bh * T + qrow];
 
   const int k_end = min(T, q0 + kBMq);
   const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
@@ -189,15 +231,15 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float th;
-          float y = score_log2<CAP>(sacc[kb][r], a, &th);
+          float t2;
+          float y = score_y<MODE>(sacc[kb][r], a.sc, &t2);
           if (need_mask) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
             if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
           }
           const float p = exp2_fast(y - lse2);
           float ds = p * (pacc[kb][r] - Di);
-          if constexpr (CAP) ds *= (1.f - th * th);
+          if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
           sacc[kb][r] = ds;
         }
       bf16x8 dsb[2][2];
@@ -221,18 +263,8 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
     cur ^= 1;
   }
 
-  if (qi < T) {
-    const int64_t row = (int64_t)bh * T + qi;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float v4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = dqacc[db][4 * i4 + j] * a.scale;
-        store_grad_rowpart<D>(a.dq, row, D, 32 * db + 8 * i4 + 4 * gl, v4, a.grad_f32 != 0);
-      }
-  }
+  finish_grad_row<D>(dqacc, a.scale, a.q + rowoff, a.dq + rowoff, qrow, gl, a.pro != 0, a.rp,
+                     qi < T);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -241,7 +273,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
 constexpr int kBNkv = 128;  // keys per dkdv workgroup
 constexpr int kBMt = 64;    // queries per dkdv tile
 
-template <int D, bool CAP>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
@@ -263,15 +295,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kwg0 = kt * kBNkv;
   const int kw0 = kwg0 + 32 * w;
   const int kj = kw0 + lr;
+  const int krow = min(kj, T - 1);
   const int window = a.window;
+  const int64_t krowoff = ((int64_t)bg * T + krow) * D;
+  const bf16* qsrc = a.pro ? a.qh : a.q;
 
   bf16x8 bk[NS], bv[NS];
   {
-    const int64_t off = ((int64_t)bg * T + min(kj, T - 1)) * D + 8 * gl;
+    const int64_t off = krowoff + 8 * gl;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       bk[s] = ld16<bf16x8>(a.k + off + 16 * s);
       bv[s] = ld16<bf16x8>(a.v + off + 16 * s);
+    }
+    if (a.pro) {
+      float x[NS][8];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) x[s][p] = (float)bk[s][p];
+      prologue_oplayout<NS>(x, krow, gl, a.rp, D);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) bk[s][p] = to_bf16(x[s][p]);
     }
   }
 
@@ -295,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int row = idx / CPR, col = (idx - row * CPR) * 8;
       const int qq = q0 + row;
       if (qq < T) {
-        rq[c] = ld16<uint4>(a.q + (hbase + qq) * D + col);
+        rq[c] = ld16<uint4>(qsrc + (hbase + qq) * D + col);
         ro[c] = ld16<uint4>(a.dO + (hbase + qq) * D + col);
       } else {
         rq[c] = make_uint4(0, 0, 0, 0);
@@ -376,15 +423,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 4 * i4 + j;
-            float th;
-            float y = score_log2<CAP>(sacc[r], a, &th);
+            float t2;
+            float y = score_y<MODE>(sacc[r], a.sc, &t2);
             if (need_mask) {
               const int iq = q0 + qloc + j;
               if (kj > iq || (window > 0 && iq - kj >= window)) y = kNegBig;
             }
             const float p = exp2_fast(y - l4[j]);
             float ds = p * (pacc[r] - d4[j]);
-            if constexpr (CAP) ds *= (1.f - th * th);
+            if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
             sacc[r] = p;
             pacc[r] = ds;
           }
@@ -409,76 +456,79 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     cur ^= 1;
   }
 
+  finish_grad_row<D>(dkacc, a.scale, a.k + krowoff, a.dk + krowoff, krow, gl, a.pro != 0, a.rp,
+                     kj < T);
   if (kj < T) {
-    const int64_t row = (int64_t)bg * T + kj;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        float k4[4], v4[4];
+        float v4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          k4[j] = dkacc[db][4 * i4 + j] * a.scale;
-          v4[j] = dvacc[db][4 * i4 + j];
-        }
-        const int col = 32 * db + 8 * i4 + 4 * gl;
-        store_grad_rowpart<D>(a.dk, row, D, col, k4, a.grad_f32 != 0);
-        store_grad_rowpart<D>(a.dv, row, D, col, v4, false);
+        for (int j = 0; j < 4; ++j) v4[j] = dvacc[db][4 * i4 + j];
+        store4(a.dv + krowoff + 32 * db + 8 * i4 + 4 * gl, v4);
       }
   }
 }
 
-BwdArgs make_args(const BwdParams& p) {
+BwdArgs make_args(const BwdParams& p, int D) {
   BwdArgs a;
   a.q = (const bf16*)p.q;
   a.k = (const bf16*)p.k;
+  a.kh = (const bf16*)p.kh;
+  a.qh = (bf16*)p.qh;
   a.v = (const bf16*)p.v;
+  a.o = (const bf16*)p.o;
   a.dO = (const bf16*)p.dO;
   a.lse = p.lse;
   a.Dvec = p.Dvec;
-  a.dq = p.dq;
-  a.dk = p.dk;
+  a.dq = (bf16*)p.dq;
+  a.dk = (bf16*)p.dk;
   a.dv = (bf16*)p.dv;
-  a.grad_f32 = p.grad_f32;
   a.B = p.B;
   a.T = p.T;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.window = p.window;
   a.ntiles = 0;
+  a.pro = (p.rope || p.qk_norm) ? 1 : 0;
   a.scale = p.scale;
-  a.scale_log2 = p.scale * kLog2e;
-  const bool cap = p.softcap > 0.f;
-  a.cap_k1 = cap ? 2.f * p.scale * kLog2e / p.softcap : 0.f;
-  a.cap_k2 = cap ? p.softcap * kLog2e : 0.f;
+  a.sc = make_score_setup(p.scale, p.softcap, D, p.qk_norm).coef;
+  a.rp = make_row_prologue(p.rope, p.rope_base, p.qk_norm, p.eps, D);
   return a;
 }
 
 template <int D>
 hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
-  BwdArgs a = make_args(p);
+  BwdArgs a = make_args(p, D);
   a.ntiles = (p.T + kBMq - 1) / kBMq;
+  const int mode = make_score_setup(p.scale, p.softcap, D, p.qk_norm).mode;
   const dim3 grid((unsigned)(a.ntiles * p.B * p.Hq));
   static const char* names[4] = {"bwd_dq_d32", "bwd_dq_d64", "bwd_dq_d96", "bwd_dq_d128"};
   TraceScope t(names[D / 32 - 1], s);
-  if (p.softcap > 0.f)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(256), 0, s, a);
+  if (mode == kScoreScale)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreScale>), grid, dim3(256), 0, s, a);
+  else if (mode == kScoreCapPoly)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapExp>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dkdv_d(const BwdParams& p, hipStream_t s) {
-  BwdArgs a = make_args(p);
+  BwdArgs a = make_args(p, D);
   a.ntiles = (p.T + kBNkv - 1) / kBNkv;
+  const int mode = make_score_setup(p.scale, p.softcap, D, p.qk_norm).mode;
   const dim3 grid((unsigned)(a.ntiles * p.B * p.Hkv));
   static const char* names[4] = {"bwd_dkdv_d32", "bwd_dkdv_d64", "bwd_dkdv_d96", "bwd_dkdv_d128"};
   TraceScope t(names[D / 32 - 1], s);
-  if (p.softcap > 0.f)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, dim3(256), 0, s, a);
+  if (mode == kScoreScale)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale>), grid, dim3(256), 0, s, a);
+  else if (mode == kScoreCapPoly)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -54,6 +54,18 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
   return r;
 }
 
+// Sum of the 8 bf16 values with fp32 accumulation (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
+  }
+  return s;
+}
+
 // Two transposing LDS reads (rows k0..k0+3 and k1..k1+3) glued into one MFMA operand.
 __device__ __forceinline__ bf16x8 tr_read_pair(const bf16* p0, const bf16* p1) {
   i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
@@ -91,6 +103,140 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int i, int D, double log2_
   const double two_pi = 6.283185307179586;
   a -= two_pi * rint(a / two_pi);
   sincosf((float)a, s, c);
+}
+
+// ---- score transform -------------------------------------------------------------------
+// The kernels work with y = S * log2(e) so that softmax weights are exp2(y - shift).
+//   kScoreScale: y = acc * scale * log2(e)
+//   kScoreCapExp: soft-cap through tanh(x) = 1 - 2 / (exp(2x) + 1) (any argument range)
+//   kScoreCapPoly: soft-cap through the odd Taylor polynomial of tanh up to x^9, used only
+//     when the host has shown |S_pre / c| <= 1/4 (QK-norm bounds |S_pre| <= scale * D);
+//     there its truncation error is below 1e-8 relative, under fp32 rounding.
+enum { kScoreScale = 0, kScoreCapExp = 1, kScoreCapPoly = 2 };
+
+struct ScoreCoef {
+  float k0;          // kScoreScale: scale*log2e;  kScoreCapExp: 2*scale*log2e/c
+  float k1;          // kScoreCapExp: c*log2e
+  float p1, p3, p5, p7, p9;  // kScoreCapPoly: y = a * (p1 + a^2 (p3 + a^2 (p5 + ...)))
+  float inv_k1_sq;   // 1 / (c log2e)^2 : tanh^2 = (y / (c log2e))^2
+};
+
+// Returns y (log2 units, unshifted); *u2 receives (y / (c log2e))^2 = tanh^2 when capped.
+template <int MODE>
+__device__ __forceinline__ float score_y(float acc, const ScoreCoef& c, float* t2) {
+  if constexpr (MODE == kScoreScale) {
+    *t2 = 0.f;
+    return acc * c.k0;
+  } else if constexpr (MODE == kScoreCapExp) {
+    const float e = exp2_fast(acc * c.k0);
+    const float th = 1.f - 2.f * rcp_fast(e + 1.f);
+    *t2 = th * th;
+    return c.k1 * th;
+  } else {
+    const float a2 = acc * acc;
+    float q = fmaf(a2, c.p9, c.p7);
+    q = fmaf(a2, q, c.p5);
+    q = fmaf(a2, q, c.p3);
+    q = fmaf(a2, q, c.p1);
+    const float y = acc * q;
+    *t2 = y * y * c.inv_k1_sq;
+    return y;
+  }
+}
+
+// ---- RoPE / RMSNorm on register-resident rows ------------------------------------------
+// Rows are held as x[NC][W]: chunk c, element e covers head-dim index d(c, e).  A lane pair
+// (l, l ^ 32) holds one full row; RoPE partners d and d + D/2 always sit in the same lane
+// (both MFMA layouts put them at chunk c and c + NC/2), so the rotation needs no exchange
+// and the RMSNorm mean is a per-lane sum plus one pair_sum.
+// omega_rev[i] = base^(-2i/D) / (2 pi): the rotation in revolutions per position.
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, int pos, double omega_rev,
+                                          bool inverse) {
+  double r = (double)pos * omega_rev;
+  r -= floor(r);
+  const float rf = (float)r;
+  const float c = __builtin_amdgcn_cosf(rf);
+  const float s = inverse ? -__builtin_amdgcn_sinf(rf) : __builtin_amdgcn_sinf(rf);
+  const float y1 = x1 * c - x2 * s;
+  const float y2 = x1 * s + x2 * c;
+  x1 = y1;
+  x2 = y2;
+}
+
+struct RowPrologue {
+  int rope, qk_norm;
+  float eps;
+  double omega_rev[64];
+};
+
+// Prologue (RoPE at `pos`, then RMSNorm) of a row held in the MFMA operand layout: chunk s,
+// element p is head-dim index 16 s + 8 (lane / 32) + p; partner chunks are s and s + NS/2.
+template <int NS>
+__device__ __forceinline__ void prologue_oplayout(float (&x)[NS][8], int pos, int gl,
+                                                  const RowPrologue& rp, int D) {
+  if (rp.rope) {
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s)
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        rope_pair(x[s][p], x[s + NS / 2][p], pos, rp.omega_rev[16 * s + 8 * gl + p], false);
+  }
+  if (rp.qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) ss = fmaf(x[s][p], x[s][p], ss);
+    ss = pair_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + rp.eps);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) x[s][p] *= inv;
+  }
+}
+
+// Gradient through the prologue for a row held in the MFMA accumulator layout: entry
+// (e, j) is head-dim index 8 e + 4 (lane / 32) + j, e < D/8; partners are e and e + D/16.
+// g holds dL/d(x^) on entry and dL/dx on exit; xr is the raw input row in the same layout.
+template <int NE>
+__device__ __forceinline__ void prologue_backward_acclayout(float (&g)[NE][4], float (&xr)[NE][4],
+                                                            int pos, int gl,
+                                                            const RowPrologue& rp, int D) {
+  if (rp.rope) {
+#pragma unroll
+    for (int e = 0; e < NE / 2; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        rope_pair(xr[e][j], xr[e + NE / 2][j], pos, rp.omega_rev[8 * e + 4 * gl + j], false);
+  }
+  if (rp.qk_norm) {
+    // y = rotated row, y^ = y / r, dy = (dy^ - y^ mean(dy^ y^)) / r
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss = fmaf(xr[e][j], xr[e][j], ss);
+    ss = pair_sum(ss);
+    const float inv_r = 1.0f / sqrtf(ss / (float)D + rp.eps);
+    float md = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) md = fmaf(g[e][j], xr[e][j] * inv_r, md);
+    md = pair_sum(md) / (float)D;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[e][j] = (g[e][j] - xr[e][j] * inv_r * md) * inv_r;
+  }
+  if (rp.rope) {
+#pragma unroll
+    for (int e = 0; e < NE / 2; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        rope_pair(g[e][j], g[e + NE / 2][j], pos, rp.omega_rev[8 * e + 4 * gl + j], true);
+  }
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -32,15 +32,16 @@ struct FwdArgs {
   bf16* o;
   float* lse;
   int B, T, Hq, Hkv, window, nqt;
-  float scale_log2;  // scale * log2(e)
-  float cap_k1;      // 2 * scale * log2(e) / c : tanh(x) = 1 - 2 / (2^(S * cap_k1) + 1)
-  float cap_k2;      // c * log2(e)
+  float shift;  // fixed softmax shift (log2 units) when the score bound allows one
+  ScoreCoef sc;
+  RowPrologue rp;
 };
 
 constexpr int kBM = 128;  // queries per workgroup
 constexpr int kBN = 64;   // keys per tile
 
-template <int D, bool CAP>
+// MODE: score transform (kScore*); FIXED: fixed shift instead of a running maximum.
+template <int D, int MODE, bool FIXED>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int LD = D + 8;          // LDS row pitch (elements)
   constexpr int NS = D / 16;         // MFMA k-steps over the head dimension
@@ -62,17 +63,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gl = l >> 5, lr = l & 31;
   const int q0 = qt * kBM, qw0 = q0 + 32 * w;
   const int qi = qw0 + lr;
+  const int qrow = min(qi, T - 1);
   const int window = a.window;
 
   const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * T * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
 
-  // Q operand: lane holds Q[qi][16 s + 8 gl .. +7].
+  // Q operand: lane holds q^[qi][16 s + 8 gl .. +7]; RoPE and RMSNorm are applied here.
   bf16x8 bq[NS];
   {
-    const bf16* qp = a.q + ((int64_t)bh * T + min(qi, T - 1)) * D + 8 * gl;
+    const bf16* qp = a.q + ((int64_t)bh * T + qrow) * D + 8 * gl;
 #pragma unroll
     for (int s = 0; s < NS; ++s) bq[s] = ld16<bf16x8>(qp + 16 * s);
+    if (a.rp.rope | a.rp.qk_norm) {
+      float x[NS][8];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) x[s][p] = (float)bq[s][p];
+      prologue_oplayout<NS>(x, qrow, gl, a.rp, D);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) bq[s][p] = to_bf16(x[s][p]);
+    }
   }
 
   const int k_end = min(T, q0 + kBM);
@@ -106,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  float m_run = kNegBig, l_run = 0.f;
+  float m_run = FIXED ? a.shift : kNegBig, l_run = 0.f;
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -115,6 +129,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const bool wave_active = qw0 < T;
   const int qw_last = min(qw0 + 31, T - 1);
+  const int trow = 4 * gl + ((l & 15) >> 2);
+  const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
   gload(kt0);
   sstore(0);
@@ -140,54 +156,62 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
           sacc[kb] = mfma32(ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl), bq[s],
                             sacc[kb]);
       }
-      float mx = kNegBig;
+      float m_new = m_run;
+      if constexpr (!FIXED) {
+        float mx = kNegBig;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float t2;
+            float y = score_y<MODE>(sacc[kb][r], a.sc, &t2);
+            if (need_mask) {
+              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
+              if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
+            }
+            sacc[kb][r] = y;
+            mx = fmaxf(mx, y);
+          }
+        mx = pair_max(mx);
+        m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = sacc[kb][r];
           float y;
-          if constexpr (CAP) {
-            const float e = exp2_fast(x * a.cap_k1);
-            y = a.cap_k2 * (1.f - 2.f * rcp_fast(e + 1.f));
+          if constexpr (FIXED) {
+            float t2;
+            y = score_y<MODE>(sacc[kb][r], a.sc, &t2);
+            if (need_mask) {
+              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
+              if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
+            }
           } else {
-            y = x * a.scale_log2;
+            y = sacc[kb][r];
           }
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
-            if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
-          }
-          sacc[kb][r] = y;
-          mx = fmaxf(mx, y);
+          sacc[kb][r] = exp2_fast(y - m_new);
         }
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);
-      m_run = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(sacc[kb][r] - m_new);
-          sacc[kb][r] = p;
-          ls += p;
-        }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       bf16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         pb[kb][0] = pack8(sacc[kb], 0);
         pb[kb][1] = pack8(sacc[kb], 8);
       }
+      // Row sum of the bf16-rounded weights, the same values the PV product uses, so that the
+      // normalisation matches the numerator exactly (a row with a single visible key returns
+      // its value row unchanged).
+      l_run += sum_bf16x8(pb[0][0]) + sum_bf16x8(pb[0][1]) + sum_bf16x8(pb[1][0]) +
+               sum_bf16x8(pb[1][1]);
       // O^T[d][q] += V^T[d][key] P^T[key][q]; lane L of each 16-lane group reads 4 values of
       // key row (k0 + L / 4) at columns 4 (L % 4) of its 16-column half.
-      const int trow = 4 * gl + ((l & 15) >> 2);
-      const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -319,17 +343,21 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   a.Hkv = p.Hkv;
   a.window = p.window;
   a.nqt = (p.T + kBM - 1) / kBM;
-  a.scale_log2 = p.scale * kLog2e;
-  const bool cap = p.softcap > 0.f;
-  a.cap_k1 = cap ? 2.f * p.scale * kLog2e / p.softcap : 0.f;
-  a.cap_k2 = cap ? p.softcap * kLog2e : 0.f;
+  const ScoreSetup ss = make_score_setup(p.scale, p.softcap, D, p.qk_norm);
+  a.shift = ss.shift;
+  a.sc = ss.coef;
+  a.rp = make_row_prologue(p.rope, p.rope_base, p.qk_norm, p.eps, D);
   const dim3 grid((unsigned)(a.nqt * p.B * p.Hq));
   static const char* names[4] = {"fwd_bf16_d32", "fwd_bf16_d64", "fwd_bf16_d96", "fwd_bf16_d128"};
   TraceScope t(names[D / 32 - 1], s);
-  if (cap)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
+  if (ss.mode == kScoreScale && ss.fixed_shift)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreScale, true>), grid, dim3(256), 0, s, a);
+  else if (ss.mode == kScoreScale)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreScale, false>), grid, dim3(256), 0, s, a);
+  else if (ss.mode == kScoreCapPoly && ss.fixed_shift)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapPoly, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapExp, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

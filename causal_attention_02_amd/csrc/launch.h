@@ -3,8 +3,11 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include "device_common.h"
 
 namespace attn {
 
@@ -16,44 +19,103 @@ struct TraceScope {
   hipStream_t stream;
 };
 
-// ---- prologue / epilogue / row reductions (rowops.hip) ----------------------------------
+// ---- score mode selection ---------------------------------------------------------------
+// With QK-norm every normalised row has |x^| <= sqrt(D), so |S_pre| <= scale * D.  When that
+// bound is small the softmax can use it as a fixed shift (exact: softmax is shift invariant,
+// and exp2(y - shift) stays far above the fp32 underflow threshold), and the soft-cap's tanh
+// argument is small enough for its Taylor polynomial.
+struct ScoreSetup {
+  int mode;          // kScoreScale / kScoreCapExp / kScoreCapPoly
+  int fixed_shift;   // 1: use `shift` instead of a running maximum (forward)
+  float shift;       // log2 units
+  ScoreCoef coef;
+};
+
+inline ScoreSetup make_score_setup(float scale, float softcap, int D, int qk_norm) {
+  ScoreSetup s{};
+  const double log2e = 1.4426950408889634;
+  // Bound with slack for the bf16 rounding of q^ and k^ (relative 2^-8 each).
+  const double bound = qk_norm ? (double)scale * D * (1.0 + 1.0 / 64) : INFINITY;
+  s.fixed_shift = bound <= 30.0;
+  s.shift = s.fixed_shift ? (float)(bound * log2e) : 0.f;
+  if (softcap <= 0.f) {
+    s.mode = kScoreScale;
+    s.coef.k0 = (float)(scale * log2e);
+  } else if (s.fixed_shift && bound / softcap <= 0.25) {
+    s.mode = kScoreCapPoly;
+    // y = c log2e tanh(a scale / c) = a * sum_k t_k (scale/c)^(2k+1) c log2e a^(2k)
+    const double x = (double)scale / softcap, k1 = (double)softcap * log2e;
+    const double t[5] = {1.0, -1.0 / 3, 2.0 / 15, -17.0 / 315, 62.0 / 2835};
+    double pw = x;
+    float* p[5] = {&s.coef.p1, &s.coef.p3, &s.coef.p5, &s.coef.p7, &s.coef.p9};
+    for (int i = 0; i < 5; ++i) {
+      *p[i] = (float)(t[i] * pw * k1);
+      pw *= x * x;
+    }
+    s.coef.k1 = (float)k1;
+    s.coef.inv_k1_sq = (float)(1.0 / (k1 * k1));
+  } else {
+    s.mode = kScoreCapExp;
+    s.coef.k0 = (float)(2.0 * scale * log2e / softcap);
+    s.coef.k1 = (float)(softcap * log2e);
+    s.coef.inv_k1_sq = (float)(1.0 / ((double)s.coef.k1 * s.coef.k1));
+  }
+  return s;
+}
+
+inline RowPrologue make_row_prologue(int rope, float rope_base, int qk_norm, float eps, int D) {
+  RowPrologue r{};
+  r.rope = rope;
+  r.qk_norm = qk_norm;
+  r.eps = eps;
+  const double two_pi = 6.283185307179586;
+  for (int i = 0; i < D / 2 && i < 64; ++i)
+    r.omega_rev[i] = rope ? pow((double)rope_base, -2.0 * i / D) / two_pi : 0.0;
+  return r;
+}
+
+// ---- row passes (rowops.hip) -------------------------------------------------------------
 // y = N(R(x)) for rows of length D; row r sits at position r % T.  elt = 2 (bf16) or 4 (f32).
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s);
-// dx = R^T(N'(dyhat)) from the fp32 gradient dyhat and the raw bf16 row x.
-hipError_t launch_epilogue(const float* dyhat, const void* x, void* dx, int64_t rows, int T, int D,
-                           int rope, float rope_base, int qk_norm, float eps, hipStream_t s);
-// Dvec[r] = sum_d dO[r, d] * O[r, d]   (bf16 rows)
-hipError_t launch_rowdot(const void* dO, const void* O, float* Dvec, int64_t rows, int D,
-                         hipStream_t s);
 
 // ---- forward (fwd.hip) -------------------------------------------------------------------
 struct FwdParams {
-  const void* q;  // [B, Hq, T, D]
-  const void* k;  // [B, Hkv, T, D]
+  const void* q;  // [B, Hq, T, D] raw q (bf16: RoPE/QK-norm applied in the kernel)
+  const void* k;  // [B, Hkv, T, D] k^ (already through the prologue)
   const void* v;
   void* o;
   float* lse;
   int B, T, Hq, Hkv, D, window;
   float scale, softcap;
+  int rope;
+  float rope_base;
+  int qk_norm;
+  float eps;
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
-hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);  // q, k already prologued
 
 // ---- backward (bwd.hip) ------------------------------------------------------------------
 struct BwdParams {
-  const void* q;     // Q^ (bf16) [B, Hq, T, D]
-  const void* k;     // K^ (bf16) [B, Hkv, T, D]
+  const void* q;     // raw q (bf16) [B, Hq, T, D]
+  const void* k;     // raw k (bf16) [B, Hkv, T, D]
+  const void* kh;    // k^ (bf16) for the dq pass (== k without RoPE/QK-norm)
+  void* qh;          // q^ (bf16) written by the dq pass for the dkdv pass (== q without them)
   const void* v;
+  const void* o;
   const void* dO;
   const float* lse;  // [B, Hq, T]
-  const float* Dvec; // [B, Hq, T]
-  void* dq;          // bf16, or fp32 when grad_f32
-  void* dk;          // bf16, or fp32 when grad_f32
-  void* dv;          // bf16
-  int grad_f32;
+  float* Dvec;       // [B, Hq, T], written by the dq pass
+  void* dq;
+  void* dk;
+  void* dv;
   int B, T, Hq, Hkv, D, window;
   float scale, softcap;
+  int rope;
+  float rope_base;
+  int qk_norm;
+  float eps;
 };
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t s);

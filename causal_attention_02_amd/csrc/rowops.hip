@@ -1,12 +1,10 @@
-// Row-wise passes around the attention core (all HBM-bound, one wave per row):
-//  * prologue: RoPE then parameter-free RMSNorm of q/k rows (nanoGPT-JAX 181M model card,
-//    "Architecture": RoPE, QK-norm, "parameter-free RMSNorm (no learnable scale)").
-//  * epilogue: the gradient through those two maps, carrying dL/d(q^) back to dL/dq.
-//  * rowdot:   D_i = sum_d dO_id * O_id, the per-row term of the softmax backward.
+// Stand-alone prologue pass: RoPE then parameter-free RMSNorm of k (and, on the fp32 path,
+// q) rows (nanoGPT-JAX 181M model card, "Architecture": RoPE, QK-norm, "parameter-free
+// RMSNorm (no learnable scale)").  HBM-bound.  The bf16 attention kernels apply the same
+// prologue to their own q rows in registers; keys are visited by many query tiles, so they
+// are prepared once here.
 //
-// RoPE pairs element i with element i + D/2 and turns the pair by p * base^(-2i/D);
-// lane i of the wave owns pair i, so the rotation needs no data exchange and the RMSNorm
-// mean is one wave reduction.
+// RoPE pairs element i with element i + D/2 and turns the pair by p * base^(-2i/D).
 #include "device_common.h"
 #include "launch.h"
 
@@ -60,99 +58,74 @@ __global__ __launch_bounds__(256) void prologue_kernel(const T* __restrict__ x, 
   }
 }
 
-__global__ __launch_bounds__(256) void epilogue_kernel(const float* __restrict__ dyhat,
-                                                       const bf16* __restrict__ x,
-                                                       bf16* __restrict__ dx, int64_t rows,
-                                                       int Tlen, int D, int rope, double log2_base,
-                                                       int qk_norm, float eps) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const int half = D >> 1;
-  const bool act = lane < half;
-  float c = 1.f, s = 0.f;
-  if (rope && act) rope_cos_sin((int)(row % Tlen), lane, D, log2_base, &c, &s);
-  float g1 = act ? dyhat[row * D + lane] : 0.f;
-  float g2 = act ? dyhat[row * D + lane + half] : 0.f;
-  if (qk_norm) {
-    // Recompute the rotated row y and its normalised form y^ = y / r.
-    const bf16* xr = x + row * D;
-    const float x1 = act ? from_bf16(xr[lane]) : 0.f;
-    const float x2 = act ? from_bf16(xr[lane + half]) : 0.f;
-    const float y1 = x1 * c - x2 * s;
-    const float y2 = x1 * s + x2 * c;
-    const float ms = wave_sum(y1 * y1 + y2 * y2) / (float)D;
-    const float inv_r = 1.0f / sqrtf(ms + eps);
-    const float h1 = y1 * inv_r, h2 = y2 * inv_r;
-    // dy = (dy^ - y^ * mean(dy^ * y^)) / r
-    const float mdot = wave_sum(g1 * h1 + g2 * h2) / (float)D;
-    g1 = (g1 - h1 * mdot) * inv_r;
-    g2 = (g2 - h2 * mdot) * inv_r;
-  }
+// bf16 rows: 8 lanes per row, each owning 8 RoPE pairs (16-byte loads of both halves).
+__global__ __launch_bounds__(256) void prologue_bf16_kernel(const bf16* __restrict__ x,
+                                                            bf16* __restrict__ y, int64_t rows,
+                                                            int Tlen, int D, RowPrologue rp) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int u = threadIdx.x & 7;
+  const bool act = row < rows && u < D / 16;
+  const int half = D / 2;
+  float x1[8], x2[8];
+  const bf16* xr = x + (row < rows ? row : 0) * D;
   if (act) {
-    // dx = R^T dy: turn the pair back by -angle.
-    const float d1 = g1 * c + g2 * s;
-    const float d2 = -g1 * s + g2 * c;
-    dx[row * D + lane] = to_bf16(d1);
-    dx[row * D + lane + half] = to_bf16(d2);
+    const bf16x8 a = ld16<bf16x8>(xr + 8 * u);
+    const bf16x8 c = ld16<bf16x8>(xr + half + 8 * u);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      x1[p] = (float)a[p];
+      x2[p] = (float)c[p];
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) x1[p] = x2[p] = 0.f;
   }
-}
-
-// 16 lanes per row, 16 rows per 256-thread block; each lane reads bf16 pairs.
-__global__ __launch_bounds__(256) void rowdot_kernel(const bf16x2* __restrict__ dO,
-                                                     const bf16x2* __restrict__ O,
-                                                     float* __restrict__ Dvec, int64_t rows,
-                                                     int D) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const int pairs = D >> 1;
-    const bf16x2* a = dO + row * pairs;
-    const bf16x2* b = O + row * pairs;
-    for (int p = sub; p < pairs; p += 16) {
-      const bf16x2 u = a[p], w = b[p];
-      acc += (float)u[0] * (float)w[0] + (float)u[1] * (float)w[1];
+  if (rp.rope && act) {
+    const int pos = (int)(row % Tlen);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) rope_pair(x1[p], x2[p], pos, rp.omega_rev[8 * u + p], false);
+  }
+  if (rp.qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) ss += x1[p] * x1[p] + x2[p] * x2[p];
+    ss += __shfl_xor(ss, 1, 8);
+    ss += __shfl_xor(ss, 2, 8);
+    ss += __shfl_xor(ss, 4, 8);
+    const float inv = 1.0f / sqrtf(ss / (float)D + rp.eps);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      x1[p] *= inv;
+      x2[p] *= inv;
     }
   }
+  if (act) {
+    bf16x8 a, c;
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (row < rows && sub == 0) Dvec[row] = acc;
+    for (int p = 0; p < 8; ++p) {
+      a[p] = to_bf16(x1[p]);
+      c[p] = to_bf16(x2[p]);
+    }
+    bf16* yr = y + row * D;
+    *reinterpret_cast<bf16x8*>(yr + 8 * u) = a;
+    *reinterpret_cast<bf16x8*>(yr + half + 8 * u) = c;
+  }
 }
 
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const double log2_base = rope ? log2((double)rope_base) : 0.0;
-  const dim3 grid((unsigned)((rows + 3) / 4));
   if (elt == 2) {
     TraceScope t("prologue_bf16", s);
-    hipLaunchKernelGGL(prologue_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (bf16*)y,
-                       rows, T, D, rope, log2_base, qk_norm, eps);
+    hipLaunchKernelGGL(prologue_bf16_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s,
+                       (const bf16*)x, (bf16*)y, rows, T, D,
+                       make_row_prologue(rope, rope_base, qk_norm, eps, D));
   } else {
+    const double log2_base = rope ? log2((double)rope_base) : 0.0;
     TraceScope t("prologue_f32", s);
-    hipLaunchKernelGGL(prologue_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (float*)y,
-                       rows, T, D, rope, log2_base, qk_norm, eps);
+    hipLaunchKernelGGL(prologue_kernel<float>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                       (const float*)x, (float*)y, rows, T, D, rope, log2_base, qk_norm, eps);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_epilogue(const float* dyhat, const void* x, void* dx, int64_t rows, int T, int D,
-                           int rope, float rope_base, int qk_norm, float eps, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const double log2_base = rope ? log2((double)rope_base) : 0.0;
-  TraceScope t("epilogue_bf16", s);
-  hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, dyhat,
-                     (const bf16*)x, (bf16*)dx, rows, T, D, rope, log2_base, qk_norm, eps);
-  return hipGetLastError();
-}
-
-hipError_t launch_rowdot(const void* dO, const void* O, float* Dvec, int64_t rows, int D,
-                         hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  TraceScope t("rowdot_bf16", s);
-  hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
-                     (const bf16x2*)dO, (const bf16x2*)O, Dvec, rows, D);
   return hipGetLastError();
 }
 

@@ -64,8 +64,10 @@ def test_workspace_sizes(L):
     c = cfg(B=16, T=2048)
     rows = 16 * 8 * 2048
     q_elems, k_elems = rows * 96, 16 * 4 * 2048 * 96
-    assert L.attn_fwd_workspace_bytes(ctypes.byref(c)) == q_elems * 2 + k_elems * 2
-    assert L.attn_bwd_workspace_bytes(ctypes.byref(c)) == rows * 4 + (q_elems + k_elems) * 6
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(c)) == k_elems * 2
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(B=16, T=2048, dtype=bd.ATTN_F32))) == \
+        (q_elems + k_elems) * 4
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(c)) == rows * 4 + (q_elems + k_elems) * 2
     plain = cfg(B=16, T=2048, opts=bd.AttnOptions())
     assert L.attn_fwd_workspace_bytes(ctypes.byref(plain)) == 0
     assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == rows * 4
