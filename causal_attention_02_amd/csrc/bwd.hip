@@ -24,6 +24,8 @@
 //    dV^T += dO^T P and dK^T += q^T dS need for their B operands; the transposed A operands
 //    come from ds_read_b64_tr_b16.  dK and dV of a KV head are summed over its query group
 //    inside the workgroup.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
   const int qi = qw0 + lr;
   const int qrow = min(qi, T - 1);
   const int window = a.window;
+  const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
   const bf16* kbase = a.kh + (int64_t)(b * a.Hkv + g) * T * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
   const int64_t rowoff = ((int64_t)bh * T + qrow) * D;
@@ -160,6 +163,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
   const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_begin / kBNk, kt1 = (k_end - 1) / kBNk;
 
+  // Rows past T are clamped to row T - 1: finite data that the causal mask removes.
   uint4 rk[CPT], rv[CPT];
   auto gload = [&](int kt) {
     const int k0 = kt * kBNk;
@@ -167,14 +171,9 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + 256 * c;
       const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      const int key = k0 + row;
-      if (key < T) {
-        rk[c] = ld16<uint4>(kbase + (int64_t)key * D + col);
-        rv[c] = ld16<uint4>(vbase + (int64_t)key * D + col);
-      } else {
-        rk[c] = make_uint4(0, 0, 0, 0);
-        rv[c] = make_uint4(0, 0, 0, 0);
-      }
+      const int64_t off = (int64_t)min(k0 + row, T - 1) * D + col;
+      rk[c] = ld16<uint4>(kbase + off);
+      rv[c] = ld16<uint4>(vbase + off);
     }
   };
   auto sstore = [&](int buf) {
@@ -212,51 +211,54 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
       const bool need_mask = (k0 + kBNk - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
       const bf16* sk = sK[cur];
       const bf16* sv = sV[cur];
-      f32x16 sacc[2], pacc[2];
+      // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
+      const int qd = qi - k0 - 4 * gl;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // S^T = K q^T and dP^T = V dO^T for this 32-key block (two interleaved chains).
+        f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sacc[kb][r] = 0.f;
-          pacc[kb][r] = 0.f;
+          sacc[r] = 0.f;
+          pacc[r] = 0.f;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int off = (kb * 32 + lr) * LD + 16 * s + 8 * gl;
-          sacc[kb] = mfma32(ld16<bf16x8>(sk + off), bq[s], sacc[kb]);
-          pacc[kb] = mfma32(ld16<bf16x8>(sv + off), bdo[s], pacc[kb]);
+          const bf16x8 ka = ld16<bf16x8>(sk + off);
+          const bf16x8 va = ld16<bf16x8>(sv + off);
+          sacc = mfma32(ka, bq[s], sacc);
+          pacc = mfma32(va, bdo[s], pacc);
         }
-      }
+        auto grads = [&](auto masked) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t2;
-          float y = score_y<MODE>(sacc[kb][r], a.sc, &t2);
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
-            if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
+          for (int r = 0; r < 16; ++r) {
+            float t2;
+            float y = score_y<MODE, MODE != kScoreScale>(sacc[r], a.sc, lse2, &t2);
+            if constexpr (decltype(masked)::value)
+              y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
+            float p = exp2_fast(y);
+            if constexpr (MODE != kScoreScale) p *= (1.f - t2);
+            sacc[r] = p * (pacc[r] - Di);
           }
-          const float p = exp2_fast(y - lse2);
-          float ds = p * (pacc[kb][r] - Di);
-          if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
-          sacc[kb][r] = ds;
-        }
-      bf16x8 dsb[2][2];
+        };
+        if (need_mask)
+          grads(std::true_type{});
+        else
+          grads(std::false_type{});
+        const bf16x8 dsb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        dsb[kb][0] = pack8(sacc[kb], 0);
-        dsb[kb][1] = pack8(sacc[kb], 8);
-      }
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 kt_[NDB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int db = 0; db < NDB; ++db) {
             const bf16* p0 = sk + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-            dqacc[db] = mfma32(tr_read_pair(p0, p0 + 8 * LD), dsb[kb][t], dqacc[db]);
+            kt_[db] = tr_read_pair(p0, p0 + 8 * LD);
           }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(kt_[db], dsb[t], dqacc[db]);
+        }
+      }
     }
     if (has_next) sstore(cur ^ 1);
     __syncthreads();
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kj = kw0 + lr;
   const int krow = min(kj, T - 1);
   const int window = a.window;
+  const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
   const int64_t krowoff = ((int64_t)bg * T + krow) * D;
   const bf16* qsrc = a.pro ? a.qh : a.q;
 
@@ -329,6 +332,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = qt1 - qt0 + 1;
   const int nit = G * nq;
 
+  // Query rows past T are clamped to row T - 1; their LSE is set to +huge so P = 0.
   uint4 rq[CPT], ro[CPT];
   float rl = 0.f, rd = 0.f;
   auto gload = [&](int it) {
@@ -340,18 +344,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + 256 * c;
       const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      const int qq = q0 + row;
-      if (qq < T) {
-        rq[c] = ld16<uint4>(qsrc + (hbase + qq) * D + col);
-        ro[c] = ld16<uint4>(a.dO + (hbase + qq) * D + col);
-      } else {
-        rq[c] = make_uint4(0, 0, 0, 0);
-        ro[c] = make_uint4(0, 0, 0, 0);
-      }
+      const int64_t off = (hbase + min(q0 + row, T - 1)) * D + col;
+      rq[c] = ld16<uint4>(qsrc + off);
+      ro[c] = ld16<uint4>(a.dO + off);
     }
     if (tid < kBMt) {
       const int qq = q0 + tid;
-      rl = qq < T ? a.lse[hbase + qq] * kLog2e : -kNegBig;  // rows past T: P = 0
+      rl = qq < T ? a.lse[hbase + qq] * kLog2e : -kNegBig;
     } else if (tid < 2 * kBMt) {
       const int qq = q0 + tid - kBMt;
       rd = qq < T ? a.Dvec[hbase + qq] : 0.f;
@@ -401,8 +400,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bool need_mask = (q0 < kw_last) || (window > 0 && q_last - kw0 >= window);
       const bf16* sq = sQ[cur];
       const bf16* so = sO[cur];
+      // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
+      const int kd = q0 + 4 * gl - kj;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        // S = q^ k^T and dP = dO V^T for 32 queries x this wave's 32 keys.
         f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -412,43 +414,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int off = (qb * 32 + lr) * LD + 16 * s + 8 * gl;
-          sacc = mfma32(ld16<bf16x8>(sq + off), bk[s], sacc);
-          pacc = mfma32(ld16<bf16x8>(so + off), bv[s], pacc);
+          const bf16x8 qa = ld16<bf16x8>(sq + off);
+          const bf16x8 oa = ld16<bf16x8>(so + off);
+          sacc = mfma32(qa, bk[s], sacc);
+          pacc = mfma32(oa, bv[s], pacc);
         }
+        f32x4 l4[4], d4[4];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int qloc = qb * 32 + 8 * i4 + 4 * gl;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[cur][qloc]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[cur][qloc]);
+          l4[i4] = *reinterpret_cast<const f32x4*>(&sL[cur][qloc]);
+          d4[i4] = *reinterpret_cast<const f32x4*>(&sD[cur][qloc]);
+        }
+        auto grads = [&](auto masked) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * i4 + j;
+          for (int r = 0; r < 16; ++r) {
             float t2;
-            float y = score_y<MODE>(sacc[r], a.sc, &t2);
-            if (need_mask) {
-              const int iq = q0 + qloc + j;
-              if (kj > iq || (window > 0 && iq - kj >= window)) y = kNegBig;
-            }
-            const float p = exp2_fast(y - l4[j]);
-            float ds = p * (pacc[r] - d4[j]);
+            float y = score_y<MODE, MODE != kScoreScale>(sacc[r], a.sc, l4[r >> 2][r & 3], &t2);
+            if constexpr (decltype(masked)::value)
+              y = visible(kd + 32 * qb + 8 * (r >> 2) + (r & 3), wlim) ? y : kNegBig;
+            const float p = exp2_fast(y);
+            float ds = p * (pacc[r] - d4[r >> 2][r & 3]);
             if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
             sacc[r] = p;
             pacc[r] = ds;
           }
-        }
+        };
+        if (need_mask)
+          grads(std::true_type{});
+        else
+          grads(std::false_type{});
         bf16x8 pb[2], dsb[2];
         pb[0] = pack8(sacc, 0);
         pb[1] = pack8(sacc, 8);
         dsb[0] = pack8(pacc, 0);
         dsb[1] = pack8(pacc, 8);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 ot[NDB], qt_[NDB];
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int db = 0; db < NDB; ++db) {
             const int off = (qb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-            dvacc[db] = mfma32(tr_read_pair(so + off, so + off + 8 * LD), pb[t], dvacc[db]);
-            dkacc[db] = mfma32(tr_read_pair(sq + off, sq + off + 8 * LD), dsb[t], dkacc[db]);
+            ot[db] = tr_read_pair(so + off, so + off + 8 * LD);
+            qt_[db] = tr_read_pair(sq + off, sq + off + 8 * LD);
           }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dvacc[db] = mfma32(ot[db], pb[t], dvacc[db]);
+            dkacc[db] = mfma32(qt_[db], dsb[t], dkacc[db]);
+          }
+        }
       }
     }
     if (has_next) sstore(cur ^ 1);

@@ -121,27 +121,40 @@ struct ScoreCoef {
   float inv_k1_sq;   // 1 / (c log2e)^2 : tanh^2 = (y / (c log2e))^2
 };
 
-// Returns y (log2 units, unshifted); *u2 receives (y / (c log2e))^2 = tanh^2 when capped.
-template <int MODE>
-__device__ __forceinline__ float score_y(float acc, const ScoreCoef& c, float* t2) {
+// Returns y - shift (log2 units).  With T2 also *t2 = tanh^2(S_pre / c) (capped modes).
+template <int MODE, bool T2>
+__device__ __forceinline__ float score_y(float acc, const ScoreCoef& c, float shift, float* t2) {
   if constexpr (MODE == kScoreScale) {
-    *t2 = 0.f;
-    return acc * c.k0;
+    if constexpr (T2) *t2 = 0.f;
+    return fmaf(acc, c.k0, -shift);
   } else if constexpr (MODE == kScoreCapExp) {
     const float e = exp2_fast(acc * c.k0);
-    const float th = 1.f - 2.f * rcp_fast(e + 1.f);
-    *t2 = th * th;
-    return c.k1 * th;
+    const float r = rcp_fast(e + 1.f);  // tanh = 1 - 2 r
+    if constexpr (T2) {
+      const float th = fmaf(r, -2.f, 1.f);
+      *t2 = th * th;
+    }
+    return fmaf(r, -2.f * c.k1, c.k1 - shift);
   } else {
     const float a2 = acc * acc;
     float q = fmaf(a2, c.p9, c.p7);
     q = fmaf(a2, q, c.p5);
     q = fmaf(a2, q, c.p3);
     q = fmaf(a2, q, c.p1);
-    const float y = acc * q;
-    *t2 = y * y * c.inv_k1_sq;
-    return y;
+    if constexpr (T2) {
+      const float u = acc * q;
+      *t2 = u * u * c.inv_k1_sq;
+      return u - shift;
+    } else {
+      return fmaf(acc, q, -shift);
+    }
   }
+}
+
+// Visibility of key j to query i as one unsigned compare: 0 <= i - j < wlim, with
+// wlim = W for a sliding window and 2^31 - 1 for plain causal attention.
+__device__ __forceinline__ bool visible(int i_minus_j, unsigned wlim) {
+  return (unsigned)i_minus_j < wlim;
 }
 
 // ---- RoPE / RMSNorm on register-resident rows ------------------------------------------

@@ -18,6 +18,8 @@
 //     accumulators straight into the B operand of O^T += V^T P^T (no LDS round trip).
 //   * Key tiles wholly above the diagonal or outside the window are never visited; only
 //     tiles that straddle a mask edge evaluate the element mask.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int qi = qw0 + lr;
   const int qrow = min(qi, T - 1);
   const int window = a.window;
+  const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
 
   const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * T * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
@@ -93,6 +96,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_begin / kBN, kt1 = (k_end - 1) / kBN;
 
+  // Tile loads: rows past T are clamped to row T - 1 (finite data whose scores the causal
+  // mask removes, since such keys lie after every query).
   uint4 rk[CPT], rv[CPT];
   auto gload = [&](int kt) {
     const int k0 = kt * kBN;
@@ -100,14 +105,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + 256 * c;
       const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      const int key = k0 + row;
-      if (key < T) {
-        rk[c] = ld16<uint4>(kbase + (int64_t)key * D + col);
-        rv[c] = ld16<uint4>(vbase + (int64_t)key * D + col);
-      } else {
-        rk[c] = make_uint4(0, 0, 0, 0);
-        rv[c] = make_uint4(0, 0, 0, 0);
-      }
+      const int64_t off = (int64_t)min(k0 + row, T - 1) * D + col;
+      rk[c] = ld16<uint4>(kbase + off);
+      rv[c] = ld16<uint4>(vbase + off);
     }
   };
   auto sstore = [&](int buf) {
@@ -146,34 +146,61 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       const bool need_mask = (k0 + kBN - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
       const bf16* sk = sK[cur];
       const bf16* sv = sV[cur];
+      // S^T = K Q^T for the two 32-key blocks: operands first, then two interleaved chains.
       f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          sacc[kb] = mfma32(ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl), bq[s],
-                            sacc[kb]);
-      }
-      float m_new = m_run;
-      if constexpr (!FIXED) {
-        float mx = kNegBig;
+      {
+        bf16x8 ka[2][NS];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float t2;
-            float y = score_y<MODE>(sacc[kb][r], a.sc, &t2);
-            if (need_mask) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
-              if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
+          for (int s = 0; s < NS; ++s)
+            ka[kb][s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[kb][s], bq[s], sacc[kb]);
+      }
+      // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
+      const int qd = qi - k0 - 4 * gl;
+      if constexpr (FIXED) {
+        // y - shift, then p = 2^(y - shift): one pass, no running maximum.
+        auto weights = [&](auto masked) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
+              if constexpr (decltype(masked)::value)
+                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
+              sacc[kb][r] = exp2_fast(y);
             }
-            sacc[kb][r] = y;
-            mx = fmaxf(mx, y);
-          }
+        };
+        if (need_mask)
+          weights(std::true_type{});
+        else
+          weights(std::false_type{});
+      } else {
+        auto scores = [&](auto masked) {
+          float mx = kNegBig;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float y = score_y<MODE, false>(sacc[kb][r], a.sc, 0.f, nullptr);
+              if constexpr (decltype(masked)::value)
+                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
+              sacc[kb][r] = y;
+              mx = fmaxf(mx, y);
+            }
+          return mx;
+        };
+        float mx = need_mask ? scores(std::true_type{}) : scores(std::false_type{});
         mx = pair_max(mx);
-        m_new = fmaxf(m_run, mx);
+        const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
@@ -181,24 +208,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(sacc[kb][r] - m_new);
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float y;
-          if constexpr (FIXED) {
-            float t2;
-            y = score_y<MODE>(sacc[kb][r], a.sc, &t2);
-            if (need_mask) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * gl + (r & 3);
-              if (key > qi || (window > 0 && qi - key >= window)) y = kNegBig;
-            }
-          } else {
-            y = sacc[kb][r];
-          }
-          sacc[kb][r] = exp2_fast(y - m_new);
-        }
       bf16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -213,14 +227,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       // O^T[d][q] += V^T[d][key] P^T[key][q]; lane L of each 16-lane group reads 4 values of
       // key row (k0 + L / 4) at columns 4 (L % 4) of its 16-column half.
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 va[NDB];
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int db = 0; db < NDB; ++db) {
             const bf16* p0 = sv + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-            oacc[db] = mfma32(tr_read_pair(p0, p0 + 8 * LD), pb[kb][t], oacc[db]);
+            va[db] = tr_read_pair(p0, p0 + 8 * LD);
           }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(va[db], pb[kb][t], oacc[db]);
+        }
     }
     if (has_next) sstore(cur ^ 1);
     __syncthreads();
