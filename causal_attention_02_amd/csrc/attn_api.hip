@@ -109,7 +109,17 @@ int check_dcfg(const attn_decode_cfg* c) {
 
 float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
 
-int decode_split_len(const attn_decode_cfg* c) { return c->split_len > 0 ? c->split_len : 256; }
+// Default chunking: enough (b, kv head, head subset, chunk) workgroups to cover about 256
+// compute units even if every cache were full; one chunk per sequence when the batch alone
+// does that (then no merge pass is needed).
+int decode_split_len(const attn_decode_cfg* c) {
+  if (c->split_len > 0) return c->split_len;
+  const long units = (long)c->B * c->Hkv * (c->Hq / c->Hkv / decode_heads_per_block(c->Hq / c->Hkv, c->D));
+  const long want = units >= 256 ? 1 : (256 + units - 1) / units;
+  long len = c->Lmax > 0 ? (c->Lmax + want - 1) / want : 64;
+  len = (len + 63) / 64 * 64;
+  return (int)(len > 0 ? len : 64);
+}
 
 int decode_nsplit(const attn_decode_cfg* c) {
   const int sl = decode_split_len(c);

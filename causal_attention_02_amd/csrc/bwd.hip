@@ -213,40 +213,44 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
       const bf16* sv = sV[cur];
       // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
       const int qd = qi - k0 - 4 * gl;
+      // S^T = K q^T and dP^T = V dO^T for both 32-key blocks are issued first; the VALU work
+      // of block 0 then overlaps block 1's MFMAs and that of block 1 overlaps block 0's dQ.
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T = K q^T and dP^T = V dO^T for this 32-key block (two interleaved chains).
-        f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sacc[r] = 0.f;
-          pacc[r] = 0.f;
+          sacc[kb][r] = 0.f;
+          pacc[kb][r] = 0.f;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int off = (kb * 32 + lr) * LD + 16 * s + 8 * gl;
           const bf16x8 ka = ld16<bf16x8>(sk + off);
           const bf16x8 va = ld16<bf16x8>(sv + off);
-          sacc = mfma32(ka, bq[s], sacc);
-          pacc = mfma32(va, bdo[s], pacc);
+          sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
+          pacc[kb] = mfma32(va, bdo[s], pacc[kb]);
         }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         auto grads = [&](auto masked) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float t2;
-            float y = score_y<MODE, MODE != kScoreScale>(sacc[r], a.sc, lse2, &t2);
+            float y = score_y<MODE, MODE != kScoreScale>(sacc[kb][r], a.sc, lse2, &t2);
             if constexpr (decltype(masked)::value)
               y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
             float p = exp2_fast(y);
             if constexpr (MODE != kScoreScale) p *= (1.f - t2);
-            sacc[r] = p * (pacc[r] - Di);
+            sacc[kb][r] = p * (pacc[kb][r] - Di);
           }
         };
         if (need_mask)
           grads(std::true_type{});
         else
           grads(std::false_type{});
-        const bf16x8 dsb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
+        const bf16x8 dsb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           bf16x8 kt_[NDB];
@@ -402,23 +406,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bf16* so = sO[cur];
       // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
       const int kd = q0 + 4 * gl - kj;
+      // S = q^ k^T and dP = dO V^T for both 32-query blocks are issued first; the VALU work of
+      // block 0 then overlaps block 1's MFMAs and that of block 1 overlaps block 0's dV/dK.
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        // S = q^ k^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-        f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sacc[r] = 0.f;
-          pacc[r] = 0.f;
+          sacc[qb][r] = 0.f;
+          pacc[qb][r] = 0.f;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int off = (qb * 32 + lr) * LD + 16 * s + 8 * gl;
           const bf16x8 qa = ld16<bf16x8>(sq + off);
           const bf16x8 oa = ld16<bf16x8>(so + off);
-          sacc = mfma32(qa, bk[s], sacc);
-          pacc = mfma32(oa, bv[s], pacc);
+          sacc[qb] = mfma32(qa, bk[s], sacc[qb]);
+          pacc[qb] = mfma32(oa, bv[s], pacc[qb]);
         }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
         f32x4 l4[4], d4[4];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
@@ -430,25 +438,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float t2;
-            float y = score_y<MODE, MODE != kScoreScale>(sacc[r], a.sc, l4[r >> 2][r & 3], &t2);
+            float y = score_y<MODE, MODE != kScoreScale>(sacc[qb][r], a.sc, l4[r >> 2][r & 3], &t2);
             if constexpr (decltype(masked)::value)
               y = visible(kd + 32 * qb + 8 * (r >> 2) + (r & 3), wlim) ? y : kNegBig;
             const float p = exp2_fast(y);
-            float ds = p * (pacc[r] - d4[r >> 2][r & 3]);
+            float ds = p * (pacc[qb][r] - d4[r >> 2][r & 3]);
             if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
-            sacc[r] = p;
-            pacc[r] = ds;
+            sacc[qb][r] = p;
+            pacc[qb][r] = ds;
           }
         };
         if (need_mask)
           grads(std::true_type{});
         else
           grads(std::false_type{});
-        bf16x8 pb[2], dsb[2];
-        pb[0] = pack8(sacc, 0);
-        pb[1] = pack8(sacc, 8);
-        dsb[0] = pack8(pacc, 0);
-        dsb[1] = pack8(pacc, 8);
+        const bf16x8 pb[2] = {pack8(sacc[qb], 0), pack8(sacc[qb], 8)};
+        const bf16x8 dsb[2] = {pack8(pacc[qb], 0), pack8(pacc[qb], 8)};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           bf16x8 ot[NDB], qt_[NDB];

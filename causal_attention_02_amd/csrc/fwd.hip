@@ -42,6 +42,26 @@ struct FwdArgs {
 constexpr int kBM = 128;  // queries per workgroup
 constexpr int kBN = 64;   // keys per tile
 
+// O^T[d][q] += V^T[d][key] P^T[key][q] for one 32-key block of the LDS tile; lane L of each
+// 16-lane group reads 4 values of key row (16 t + L / 4) at columns 4 (L % 4) of its half.
+template <int D>
+__device__ __forceinline__ void pv_block(f32x16 (&oacc)[D / 32], const bf16* sv, int kb,
+                                         const bf16x8 (&pb)[2], int trow, int tcol) {
+  constexpr int LD = D + 8;
+  constexpr int NDB = D / 32;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x8 va[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16* p0 = sv + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
+      va[db] = tr_read_pair(p0, p0 + 8 * LD);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(va[db], pb[t], oacc[db]);
+  }
+}
+
 // MODE: score transform (kScore*); FIXED: fixed shift instead of a running maximum.
 template <int D, int MODE, bool FIXED>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
@@ -146,31 +166,28 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       const bool need_mask = (k0 + kBN - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
       const bf16* sk = sK[cur];
       const bf16* sv = sV[cur];
-      // S^T = K Q^T for the two 32-key blocks: operands first, then two interleaved chains.
-      f32x16 sacc[2];
-      {
-        bf16x8 ka[2][NS];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-            ka[kb][s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[kb][s], bq[s], sacc[kb]);
-      }
       // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
       const int qd = qi - k0 - 4 * gl;
-      if constexpr (FIXED) {
-        // y - shift, then p = 2^(y - shift): one pass, no running maximum.
-        auto weights = [&](auto masked) {
+      // S^T = K Q^T for the two 32-key blocks.  Both chains are issued before block 0's
+      // weights are computed, so the VALU work of block 0 overlaps the MFMAs of block 1, and
+      // that of block 1 overlaps block 0's PV product.
+      f32x16 sacc[2];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 ka[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          ka[s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[s], bq[s], sacc[kb]);
+      }
+      if constexpr (FIXED) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // p = 2^(y - shift) for this block, one pass, no running maximum.
+          auto weights = [&](auto masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
@@ -178,11 +195,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
                 y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
               sacc[kb][r] = exp2_fast(y);
             }
-        };
-        if (need_mask)
-          weights(std::true_type{});
-        else
-          weights(std::false_type{});
+          };
+          if (need_mask)
+            weights(std::true_type{});
+          else
+            weights(std::false_type{});
+          const bf16x8 pb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
+          // Row sum of the bf16-rounded weights, the values the PV product uses, so the
+          // normalisation matches the numerator exactly (a single visible key returns V).
+          l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
+          pv_block<D>(oacc, sv, kb, pb, trow, tcol);
+        }
       } else {
         auto scores = [&](auto masked) {
           float mx = kNegBig;
@@ -209,36 +232,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(sacc[kb][r] - m_new);
-      }
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pb[kb][0] = pack8(sacc[kb], 0);
-        pb[kb][1] = pack8(sacc[kb], 8);
-      }
-      // Row sum of the bf16-rounded weights, the same values the PV product uses, so that the
-      // normalisation matches the numerator exactly (a row with a single visible key returns
-      // its value row unchanged).
-      l_run += sum_bf16x8(pb[0][0]) + sum_bf16x8(pb[0][1]) + sum_bf16x8(pb[1][0]) +
-               sum_bf16x8(pb[1][1]);
-      // O^T[d][q] += V^T[d][key] P^T[key][q]; lane L of each 16-lane group reads 4 values of
-      // key row (k0 + L / 4) at columns 4 (L % 4) of its 16-column half.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 va[NDB];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16* p0 = sv + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-            va[db] = tr_read_pair(p0, p0 + 8 * LD);
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(va[db], pb[kb][t], oacc[db]);
+          const bf16x8 pb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
+          l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
+          pv_block<D>(oacc, sv, kb, pb, trow, tcol);
         }
+      }
     }
     if (has_next) sstore(cur ^ 1);
     __syncthreads();

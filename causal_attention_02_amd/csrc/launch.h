@@ -121,6 +121,14 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t s);
 
 // ---- decode (decode.hip) -----------------------------------------------------------------
+// Query heads handled by one decode workgroup: the largest of 4, 3, 2, 1 that divides the
+// group size and keeps heads x D <= 256 (the per-lane state fits in registers), so each
+// workgroup streams its KV head's cache once for all of them.
+inline int decode_heads_per_block(int group, int D) {
+  for (int h = 4; h > 1; --h)
+    if (group % h == 0 && h * D <= 256) return h;
+  return 1;
+}
 struct DecodeParams {
   const void* q;        // [B, Hq, D]
   const void* kc;       // [B, Hkv, Lmax, D]

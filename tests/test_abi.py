@@ -72,8 +72,12 @@ def test_workspace_sizes(L):
     assert L.attn_fwd_workspace_bytes(ctypes.byref(plain)) == 0
     assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == rows * 4
     assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(Hq=5))) == 0  # invalid -> 0
+    # Default chunking: 64 x 4 (b, kv head) workgroups already cover the GPU -> one chunk.
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(softcap=50.0, rope=True))
-    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 8 * 98 * 4
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 1 * 98 * 4
+    # One sequence: 4 (b, kv head) units -> 64 chunks of 64 rows over a 4096-row cache.
+    d = bd.make_decode_cfg(1, 8, 4, 96, 4096, bd.AttnOptions())
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 1 * 8 * 64 * 98 * 4
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(), split_len=128)
     assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 16 * 98 * 4
 
