@@ -352,13 +352,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       rq[c] = ld16<uint4>(qsrc + off);
       ro[c] = ld16<uint4>(a.dO + off);
     }
-    if (tid < kBMt) {
-      const int qq = q0 + tid;
-      rl = qq < T ? a.lse[hbase + qq] * kLog2e : -kNegBig;
-    } else if (tid < 2 * kBMt) {
-      const int qq = q0 + tid - kBMt;
-      rd = qq < T ? a.Dvec[hbase + qq] : 0.f;
-    }
+    // Every lane loads (no divergent loads, so the waits stay precise); the first 64 lanes
+    // of the workgroup store LSE, the next 64 D.
+    const int qq = q0 + (tid & (kBMt - 1));
+    const int64_t qc = hbase + min(qq, T - 1);
+    const float lv = a.lse[qc], dv = a.Dvec[qc];
+    rl = qq < T ? lv * kLog2e : -kNegBig;
+    rd = qq < T ? dv : 0.f;
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -406,54 +406,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bf16* so = sO[cur];
       // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
       const int kd = q0 + 4 * gl - kj;
-      // S = q^ k^T and dP = dO V^T for both 32-query blocks are issued first; the VALU work of
-      // block 0 then overlaps block 1's MFMAs and that of block 1 overlaps block 0's dV/dK.
-      f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        // S = q^ k^T and dP = dO V^T for 32 queries x this wave's 32 keys.
+        f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sacc[qb][r] = 0.f;
-          pacc[qb][r] = 0.f;
+          sacc[r] = 0.f;
+          pacc[r] = 0.f;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int off = (qb * 32 + lr) * LD + 16 * s + 8 * gl;
           const bf16x8 qa = ld16<bf16x8>(sq + off);
           const bf16x8 oa = ld16<bf16x8>(so + off);
-          sacc[qb] = mfma32(qa, bk[s], sacc[qb]);
-          pacc[qb] = mfma32(oa, bv[s], pacc[qb]);
+          sacc = mfma32(qa, bk[s], sacc);
+          pacc = mfma32(oa, bv[s], pacc);
         }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 l4[4], d4[4];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int qloc = qb * 32 + 8 * i4 + 4 * gl;
-          l4[i4] = *reinterpret_cast<const f32x4*>(&sL[cur][qloc]);
-          d4[i4] = *reinterpret_cast<const f32x4*>(&sD[cur][qloc]);
-        }
+        const float* lq = &sL[cur][qb * 32 + 4 * gl];
+        const float* dq_ = &sD[cur][qb * 32 + 4 * gl];
         auto grads = [&](auto masked) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
+            const int qo = 8 * (r >> 2) + (r & 3);  // query offset within the block
             float t2;
-            float y = score_y<MODE, MODE != kScoreScale>(sacc[qb][r], a.sc, l4[r >> 2][r & 3], &t2);
+            float y = score_y<MODE, MODE != kScoreScale>(sacc[r], a.sc, lq[qo], &t2);
             if constexpr (decltype(masked)::value)
-              y = visible(kd + 32 * qb + 8 * (r >> 2) + (r & 3), wlim) ? y : kNegBig;
+              y = visible(kd + 32 * qb + qo, wlim) ? y : kNegBig;
             const float p = exp2_fast(y);
-            float ds = p * (pacc[qb][r] - d4[r >> 2][r & 3]);
+            float ds = p * (pacc[r] - dq_[qo]);
             if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
-            sacc[qb][r] = p;
-            pacc[qb][r] = ds;
+            sacc[r] = p;
+            pacc[r] = ds;
           }
         };
         if (need_mask)
           grads(std::true_type{});
         else
           grads(std::false_type{});
-        const bf16x8 pb[2] = {pack8(sacc[qb], 0), pack8(sacc[qb], 8)};
-        const bf16x8 dsb[2] = {pack8(pacc[qb], 0), pack8(pacc[qb], 8)};
+        const bf16x8 pb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
+        const bf16x8 dsb[2] = {pack8(pacc, 0), pack8(pacc, 8)};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           bf16x8 ot[NDB], qt_[NDB];

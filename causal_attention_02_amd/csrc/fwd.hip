@@ -168,45 +168,79 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       const bf16* sv = sV[cur];
       // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
       const int qd = qi - k0 - 4 * gl;
-      // S^T = K Q^T for the two 32-key blocks.  Both chains are issued before block 0's
-      // weights are computed, so the VALU work of block 0 overlaps the MFMAs of block 1, and
-      // that of block 1 overlaps block 0's PV product.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 ka[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          ka[s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[s], bq[s], sacc[kb]);
-      }
       if constexpr (FIXED) {
+        // One straight-line body per mask variant, software-pipelined over the two 32-key
+        // blocks: block 1's score MFMAs are interleaved with block 0's weight VALU work, and
+        // block 0's PV MFMAs with block 1's (sched_group_barrier fixes the interleave).
+        auto body = [&](auto masked) {
+          constexpr bool MASKED = decltype(masked)::value;
+          f32x16 sacc[2];
+          bf16x8 ka[2][NS];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          // p = 2^(y - shift) for this block, one pass, no running maximum.
-          auto weights = [&](auto masked) {
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              ka[kb][s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[kb][s], bq[s], sacc[kb]);
+          }
+          bf16x8 pb[2][2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
-              if constexpr (decltype(masked)::value)
+              if constexpr (MASKED)
                 y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
               sacc[kb][r] = exp2_fast(y);
             }
-          };
-          if (need_mask)
-            weights(std::true_type{});
-          else
-            weights(std::false_type{});
-          const bf16x8 pb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
-          // Row sum of the bf16-rounded weights, the values the PV product uses, so the
-          // normalisation matches the numerator exactly (a single visible key returns V).
-          l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
-          pv_block<D>(oacc, sv, kb, pb, trow, tcol);
-        }
+            pb[kb][0] = pack8(sacc[kb], 0);
+            pb[kb][1] = pack8(sacc[kb], 8);
+            // Row sum of the bf16-rounded weights, the values the PV product uses, so the
+            // normalisation matches the numerator exactly (a single visible key returns V).
+            l_run += sum_bf16x8(pb[kb][0]) + sum_bf16x8(pb[kb][1]);
+            pv_block<D>(oacc, sv, kb, pb[kb], trow, tcol);
+          }
+          // Schedule: block 0 scores; block 1 scores under block 0's weights; block 0's PV
+          // under block 1's weights; block 1's PV.
+          constexpr int VW = MASKED ? 26 : 22;  // VALU ops per interleave slot
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * NS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VW, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VW * NS / (2 * NDB), 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDB, 0);
+        };
+        if (need_mask)
+          body(std::true_type{});
+        else
+          body(std::false_type{});
       } else {
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          bf16x8 ka[NS];
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            ka[s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[s], bq[s], sacc[kb]);
+        }
         auto scores = [&](auto masked) {
           float mx = kNegBig;
 #pragma unroll
