@@ -129,7 +129,8 @@ int decode_nsplit(const attn_decode_cfg* c) {
 // Workspace layouts (each region 256-byte aligned), when RoPE or QK-norm is on:
 //   fwd bf16: [k^ B*Hkv*T*D bf16]       (q gets its prologue inside the forward kernel)
 //   fwd f32:  [q^ B*Hq*T*D f32][k^ B*Hkv*T*D f32]
-//   bwd:      [D B*Hq*T f32][q^ bf16][k^ bf16]   (without RoPE/QK-norm only D)
+//   bwd:      [D B*Hq*T f32][LSE*log2e B*Hq*T f32][q^ bf16][k^ bf16]
+//             (without RoPE/QK-norm only the two f32 rows)
 size_t fwd_ws(const attn_cfg* c) {
   if (!(c->rope || c->qk_norm)) return 0;
   const size_t nq = (size_t)c->B * c->Hq * c->T * c->D, nk = (size_t)c->B * c->Hkv * c->T * c->D;
@@ -139,7 +140,7 @@ size_t fwd_ws(const attn_cfg* c) {
 
 size_t bwd_ws(const attn_cfg* c) {
   const size_t rows = (size_t)c->B * c->Hq * c->T;
-  size_t s = align_up(rows * 4);
+  size_t s = 2 * align_up(rows * 4);
   if (c->rope || c->qk_norm) {
     const size_t nq = rows * c->D, nk = (size_t)c->B * c->Hkv * c->T * c->D;
     s += align_up(nq * 2) + align_up(nk * 2);
@@ -234,6 +235,8 @@ int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, con
   char* w = (char*)ws;
   float* Dvec = (float*)w;
   w += align_up((size_t)qrows * 4);
+  float* L2 = (float*)w;
+  w += align_up((size_t)qrows * 4);
   const bool pro = c->rope || c->qk_norm;
   void* qh = const_cast<void*>(q);
   const void* kh = k;
@@ -246,7 +249,7 @@ int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, con
                         c->norm_eps, s);
     kh = kw;
   }
-  BwdParams p{q, k, kh, qh, v, o, dO, lse, Dvec, dq, dk, dv, c->B, c->T, c->Hq, c->Hkv, c->D,
+  BwdParams p{q, k, kh, qh, v, o, dO, lse, Dvec, L2, dq, dk, dv, c->B, c->T, c->Hq, c->Hkv, c->D,
               c->window, eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base,
               c->qk_norm, c->norm_eps};
   if (e == hipSuccess) e = launch_bwd_dq(p, s);

@@ -43,6 +43,7 @@ struct BwdArgs {
   const bf16* dO;
   const float* lse;
   float* Dvec;
+  float* L2;  // LSE * log2(e) per query row (written by dq for dkdv)
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -155,9 +156,10 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
       for (int p = 0; p < 8; ++p) dsum = fmaf((float)bdo[s][p], (float)ov[p], dsum);
     }
     Di = pair_sum(dsum);
-    if (gl == 0 && qi < T) a.Dvec[(int64_t)bh * T + qi] = Di;
+    if (gl == 0 && qi < T) a.Dvec[(int64_t)bh * T + qi] = -Di;
   }
   const float lse2 = a.lse[(int64_t)bh * T + qrow] * kLog2e;
+  if (gl == 0 && qi < T) a.L2[(int64_t)bh * T + qi] = lse2;
 
   const int k_end = min(T, q0 + kBMq);
   const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
@@ -218,10 +220,11 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // dP^T accumulates on top of -D_i, so it comes out as dP - D.
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           sacc[kb][r] = 0.f;
-          pacc[kb][r] = 0.f;
+          pacc[kb][r] = -Di;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -237,13 +240,13 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
         auto grads = [&](auto masked) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float t2;
-            float y = score_y<MODE, MODE != kScoreScale>(sacc[kb][r], a.sc, lse2, &t2);
+            float gf;
+            float y = score_grad<MODE>(sacc[kb][r], a.sc, lse2, &gf);
             if constexpr (decltype(masked)::value)
               y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
             float p = exp2_fast(y);
-            if constexpr (MODE != kScoreScale) p *= (1.f - t2);
-            sacc[kb][r] = p * (pacc[kb][r] - Di);
+            if constexpr (MODE != kScoreScale) p *= gf;
+            sacc[kb][r] = p * pacc[kb][r];
           }
         };
         if (need_mask)
@@ -279,17 +282,53 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
 constexpr int kBNkv = 128;  // keys per dkdv workgroup
 constexpr int kBMt = 64;    // queries per dkdv tile
 
+// Direct global -> LDS copies of 64-row bf16 tiles into LDS rows of pitch D + 8 elements
+// (the pad keeps the row-per-lane MFMA operand reads free of bank conflicts).  The LDS image
+// is cut into 1 KB chunks, one wave-wide 16-byte load each: lane l of chunk c carries image
+// granule p = 64 c + l, which is granule p % G of padded row p / G (G = D/8 + 1).  The
+// source tile is contiguous (rows r0 .. r0 + 63 of one head), so that granule sits
+// p - p / G granules past the tile start; sources are clamped to the head's last granule
+// (rows past the end and the pad granules read real, finite data that is never used).
+// Chunks are dealt round-robin to the NW waves; a wave keeps one offset per chunk it owns.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int G = D / 8 + 1;
+  static constexpr int NC = (G + NW - 1) / NW;  // chunks per wave (the last may be absent)
+  int rel[NC];                                  // granule offset from the tile start
+  __device__ __forceinline__ TileDma(int w, int l) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int pg = 64 * (w + NW * i) + l;
+      rel[i] = pg - pg / G;
+    }
+  }
+  // Copy rows r0.. of the head starting at src (T rows) into lds.
+  __device__ __forceinline__ void copy(bf16* lds, const bf16* src, int r0, int T, int w) const {
+    const int first = r0 * (D / 8), last = T * (D / 8) - 1;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = w + NW * i;
+      if (c < G) {
+        const bf16* from = src + 8 * (int64_t)min(first + rel[i], last);
+        __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
+      }
+    }
+  }
+};
+
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = kBMt * CPR / 256;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][kBMt * LD];
-  __shared__ __attribute__((aligned(16))) bf16 sO[2][kBMt * LD];  // dO tile
-  __shared__ __attribute__((aligned(16))) float sL[2][kBMt];      // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][kBMt];      // D = rowsum(dO * O)
+  constexpr int TILE = kBMt * LD;  // elements of one padded tile (a whole number of 1 KB)
+  static_assert(TILE % 512 == 0, "tile image must be whole 1 KB chunks");
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sO0[TILE];  // dO tiles
+  __shared__ __attribute__((aligned(16))) bf16 sO1[TILE];
+  __shared__ __attribute__((aligned(16))) float sL[2][kBMt];  // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kBMt];  // -D, D = rowsum(dO * O)
 
   const int T = a.T;
   const int nbg = a.B * a.Hkv;
@@ -303,7 +342,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kj = kw0 + lr;
   const int krow = min(kj, T - 1);
   const int window = a.window;
-  const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
+  // Query i sees this lane's key j iff 0 <= i - j < lim: the causal / window rule plus
+  // i < T (query rows past T are clamped copies of row T - 1 and must get P = 0).
+  const unsigned lim = (unsigned)min(window > 0 ? window : 0x7fffffff, max(T - kj, 0));
   const int64_t krowoff = ((int64_t)bg * T + krow) * D;
   const bf16* qsrc = a.pro ? a.qh : a.q;
 
@@ -336,42 +377,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = qt1 - qt0 + 1;
   const int nit = G * nq;
 
-  // Query rows past T are clamped to row T - 1; their LSE is set to +huge so P = 0.
-  uint4 rq[CPT], ro[CPT];
-  float rl = 0.f, rd = 0.f;
-  auto gload = [&](int it) {
+  const TileDma<D, 4> tdma(w, l);
+  // Issue the direct loads of iteration it's q^ / dO tiles and LSE / D vectors into
+  // buffer `buf`; they are waited for at the end of the iteration that issues them.
+  auto dma = [&](int it, int buf) {
     const int hh = it / nq;
     const int q0 = (qt0 + it - hh * nq) * kBMt;
-    const int h = g * G + hh;
-    const int64_t hbase = (int64_t)(b * a.Hq + h) * T;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      const int64_t off = (hbase + min(q0 + row, T - 1)) * D + col;
-      rq[c] = ld16<uint4>(qsrc + off);
-      ro[c] = ld16<uint4>(a.dO + off);
-    }
-    // Every lane loads (no divergent loads, so the waits stay precise); the first 64 lanes
-    // of the workgroup store LSE, the next 64 D.
-    const int qq = q0 + (tid & (kBMt - 1));
-    const int64_t qc = hbase + min(qq, T - 1);
-    const float lv = a.lse[qc], dv = a.Dvec[qc];
-    rl = qq < T ? lv * kLog2e : -kNegBig;
-    rd = qq < T ? dv : 0.f;
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      *reinterpret_cast<uint4*>(&sQ[buf][row * LD + col]) = rq[c];
-      *reinterpret_cast<uint4*>(&sO[buf][row * LD + col]) = ro[c];
-    }
-    if (tid < kBMt)
-      sL[buf][tid] = rl;
-    else if (tid < 2 * kBMt)
-      sD[buf][tid - kBMt] = rd;
+    const int64_t hbase = (int64_t)(b * a.Hq + g * G + hh) * T;
+    tdma.copy(buf ? sQ1 : sQ0, qsrc + hbase * D, q0, T, w);
+    tdma.copy(buf ? sO1 : sO0, a.dO + hbase * D, q0, T, w);
+    const int64_t qc = hbase + min(q0 + l, T - 1);
+    if (w == 2) __builtin_amdgcn_global_load_lds(a.L2 + qc, &sL[buf][0], 4, 0, 0);
+    if (w == 3) __builtin_amdgcn_global_load_lds(a.Dvec + qc, &sD[buf][0], 4, 0, 0);
   };
 
   f32x16 dvacc[NDB], dkacc[NDB];
@@ -388,54 +405,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  int cur = 0;
-  for (int it = 0; it < nit; ++it) {
-    const bool has_next = it + 1 < nit;
-    if (has_next) gload(it + 1);
+  // One q tile against this wave's 32 keys, operands in (sq, so, sl, sd).
+  auto step = [&](int it, const bf16* sq, const bf16* so, const float* sl, const float* sd) {
     const int hh = it / nq;
     const int q0 = (qt0 + it - hh * nq) * kBMt;
     const int q_last = min(q0 + kBMt - 1, T - 1);
-    const bool skip = !wave_active || q_last < kw0 ||
-                      (window > 0 && q0 > kw_last + window - 1);
-    if (!skip) {
-      const bool need_mask = (q0 < kw_last) || (window > 0 && q_last - kw0 >= window);
-      const bf16* sq = sQ[cur];
-      const bf16* so = sO[cur];
-      // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
-      const int kd = q0 + 4 * gl - kj;
+    const bool skip = !wave_active || q_last < kw0 || (window > 0 && q0 > kw_last + window - 1);
+    if (skip) return;
+    const bool need_mask = (q0 < kw_last) || (q0 + kBMt > T) ||
+                           (window > 0 && q_last - kw0 >= window);
+    // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
+    const int kd = q0 + 4 * gl - kj;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S = q^ k^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-        f32x16 sacc, pacc;
+    for (int qb = 0; qb < 2; ++qb) {
+      // S = q^ k^T and dP = dO V^T for 32 queries x this wave's 32 keys; dP accumulates on
+      // top of -D (element r belongs to query offset 8 (r / 4) + r % 4 of the block), so it
+      // comes out as dP - D.
+      f32x16 sacc, pacc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[r] = 0.f;
-          pacc[r] = 0.f;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float4 nd = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 8 * i);
+        pacc[4 * i] = nd.x;
+        pacc[4 * i + 1] = nd.y;
+        pacc[4 * i + 2] = nd.z;
+        pacc[4 * i + 3] = nd.w;
+      }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int off = (qb * 32 + lr) * LD + 16 * s + 8 * gl;
-          const bf16x8 qa = ld16<bf16x8>(sq + off);
-          const bf16x8 oa = ld16<bf16x8>(so + off);
-          sacc = mfma32(qa, bk[s], sacc);
-          pacc = mfma32(oa, bv[s], pacc);
-        }
-        const float* lq = &sL[cur][qb * 32 + 4 * gl];
-        const float* dq_ = &sD[cur][qb * 32 + 4 * gl];
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = (qb * 32 + lr) * LD + 16 * s + 8 * gl;
+        const bf16x8 qa = ld16<bf16x8>(sq + off);
+        const bf16x8 oa = ld16<bf16x8>(so + off);
+        sacc = mfma32(qa, bk[s], sacc);
+        pacc = mfma32(oa, bv[s], pacc);
+      }
+      // Phase fences: with two waves per SIMD the other wave fills one wave's MFMA, VALU
+      // and LDS phases, so each wave keeps only one phase's registers live.
+      __builtin_amdgcn_sched_barrier(0);
+      // Half t covers elements 8t .. 8t + 7 (queries 16t .. 16t + 15 of the block): the
+      // softmax gradient, then that half's share of dV^T += dO^T P and dK^T += q^T dS.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4 lq[2] = {*reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t),
+                              *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t + 8)};
         auto grads = [&](auto masked) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qo = 8 * (r >> 2) + (r & 3);  // query offset within the block
-            float t2;
-            float y = score_y<MODE, MODE != kScoreScale>(sacc[r], a.sc, lq[qo], &t2);
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * t + e;
+            const int qo = 8 * (r >> 2) + (r & 3);
+            float gf;
+            float y = score_grad<MODE>(sacc[r], a.sc, lq[e >> 2][e & 3], &gf);
             if constexpr (decltype(masked)::value)
-              y = visible(kd + 32 * qb + qo, wlim) ? y : kNegBig;
+              y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
             const float p = exp2_fast(y);
-            float ds = p * (pacc[r] - dq_[qo]);
-            if constexpr (MODE != kScoreScale) ds *= (1.f - t2);
+            float ds = p * pacc[r];
+            if constexpr (MODE != kScoreScale) ds *= gf;
             sacc[r] = p;
             pacc[r] = ds;
           }
@@ -444,28 +469,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           grads(std::true_type{});
         else
           grads(std::false_type{});
-        const bf16x8 pb[2] = {pack8(sacc, 0), pack8(sacc, 8)};
-        const bf16x8 dsb[2] = {pack8(pacc, 0), pack8(pacc, 8)};
+        const bf16x8 pb = pack8(sacc, 8 * t), dsb = pack8(pacc, 8 * t);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 ot[NDB], qt_[NDB];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 ot[NDB], qt_[NDB];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int off = (qb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-            ot[db] = tr_read_pair(so + off, so + off + 8 * LD);
-            qt_[db] = tr_read_pair(sq + off, sq + off + 8 * LD);
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dvacc[db] = mfma32(ot[db], pb[t], dvacc[db]);
-            dkacc[db] = mfma32(qt_[db], dsb[t], dkacc[db]);
-          }
+        for (int db = 0; db < NDB; ++db) {
+          const int off = (qb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
+          ot[db] = tr_read_pair(so + off, so + off + 8 * LD);
+          qt_[db] = tr_read_pair(sq + off, sq + off + 8 * LD);
         }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = mfma32(ot[db], pb, dvacc[db]);
+          dkacc[db] = mfma32(qt_[db], dsb, dkacc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (has_next) sstore(cur ^ 1);
+  };
+
+  // Two-deep pipeline over the (query head, query tile) iterations, unrolled by two so each
+  // LDS buffer is a distinct array: the loads into one buffer never wait on reads of the other.
+  dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) dma(it + 1, 1);
+    step(it, sQ0, sO0, sL[0], sD[0]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur ^= 1;
+    if (it + 1 >= nit) break;
+    if (it + 2 < nit) dma(it + 2, 0);
+    step(it + 1, sQ1, sO1, sL[1], sD[1]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   finish_grad_row<D>(dkacc, a.scale, a.k + krowoff, a.dk + krowoff, krow, gl, a.pro != 0, a.rp,
@@ -494,6 +531,7 @@ BwdArgs make_args(const BwdParams& p, int D) {
   a.dO = (const bf16*)p.dO;
   a.lse = p.lse;
   a.Dvec = p.Dvec;
+  a.L2 = p.L2;
   a.dq = (bf16*)p.dq;
   a.dk = (bf16*)p.dk;
   a.dv = (bf16*)p.dv;
@@ -520,6 +558,8 @@ hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
   TraceScope t(names[D / 32 - 1], s);
   if (mode == kScoreScale)
     hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreScale>), grid, dim3(256), 0, s, a);
+  else if (mode == kScoreCapPoly5)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly5>), grid, dim3(256), 0, s, a);
   else if (mode == kScoreCapPoly)
     hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly>), grid, dim3(256), 0, s, a);
   else
@@ -537,6 +577,8 @@ hipError_t launch_dkdv_d(const BwdParams& p, hipStream_t s) {
   TraceScope t(names[D / 32 - 1], s);
   if (mode == kScoreScale)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale>), grid, dim3(256), 0, s, a);
+  else if (mode == kScoreCapPoly5)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5>), grid, dim3(256), 0, s, a);
   else if (mode == kScoreCapPoly)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly>), grid, dim3(256), 0, s, a);
   else

@@ -360,6 +360,7 @@ hipError_t launch_split(const DecArgs& a, hipStream_t s) {
 template <int D, int HPB>
 hipError_t launch_split_mode(const DecArgs& a, int mode, hipStream_t s) {
   if (mode == kScoreScale) return launch_split<D, HPB, kScoreScale>(a, s);
+  if (mode == kScoreCapPoly5) return launch_split<D, HPB, kScoreCapPoly5>(a, s);
   if (mode == kScoreCapPoly) return launch_split<D, HPB, kScoreCapPoly>(a, s);
   return launch_split<D, HPB, kScoreCapExp>(a, s);
 }

@@ -112,16 +112,22 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int i, int D, double log2_
 //   kScoreCapPoly: soft-cap through the odd Taylor polynomial of tanh up to x^9, used only
 //     when the host has shown |S_pre / c| <= 1/4 (QK-norm bounds |S_pre| <= scale * D);
 //     there its truncation error is below 1e-8 relative, under fp32 rounding.
-enum { kScoreScale = 0, kScoreCapExp = 1, kScoreCapPoly = 2 };
+//   kScoreCapPoly5: the same series cut after x^5, used only where the host has shown that
+//     the dropped terms move y by at most 2^-12 (a relative change of 2^-12 in a softmax
+//     weight, an eighth of bf16's rounding step) and that the derivative series
+//     sech^2(x) = 1 - x^2 + (2/3) x^4 cut the same way is within 2^-12 relative.
+enum { kScoreScale = 0, kScoreCapExp = 1, kScoreCapPoly = 2, kScoreCapPoly5 = 3 };
 
 struct ScoreCoef {
   float k0;          // kScoreScale: scale*log2e;  kScoreCapExp: 2*scale*log2e/c
   float k1;          // kScoreCapExp: c*log2e
-  float p1, p3, p5, p7, p9;  // kScoreCapPoly: y = a * (p1 + a^2 (p3 + a^2 (p5 + ...)))
+  float p1, p3, p5, p7, p9;  // polynomial modes: y = a * (p1 + a^2 (p3 + a^2 (p5 + ...)))
   float inv_k1_sq;   // 1 / (c log2e)^2 : tanh^2 = (y / (c log2e))^2
+  float g2, g4;      // kScoreCapPoly5: sech^2 = 1 + a^2 (g2 + a^2 g4)
 };
 
-// Returns y - shift (log2 units).  With T2 also *t2 = tanh^2(S_pre / c) (capped modes).
+// Returns y - shift (log2 units).  With T2 also *t2 = tanh^2(S_pre / c) (exp / degree-9
+// modes only).
 template <int MODE, bool T2>
 __device__ __forceinline__ float score_y(float acc, const ScoreCoef& c, float shift, float* t2) {
   if constexpr (MODE == kScoreScale) {
@@ -135,6 +141,11 @@ __device__ __forceinline__ float score_y(float acc, const ScoreCoef& c, float sh
       *t2 = th * th;
     }
     return fmaf(r, -2.f * c.k1, c.k1 - shift);
+  } else if constexpr (MODE == kScoreCapPoly5) {
+    static_assert(!T2, "degree-5 mode gives the derivative through score_grad");
+    const float a2 = acc * acc;
+    const float q = fmaf(a2, fmaf(a2, c.p5, c.p3), c.p1);
+    return fmaf(acc, q, -shift);
   } else {
     const float a2 = acc * acc;
     float q = fmaf(a2, c.p9, c.p7);
@@ -148,6 +159,25 @@ __device__ __forceinline__ float score_y(float acc, const ScoreCoef& c, float sh
     } else {
       return fmaf(acc, q, -shift);
     }
+  }
+}
+
+// Backward form: returns y - shift and sets *g to d(capped score)/d(raw score) relative to
+// the uncapped slope, i.e. 1 - tanh^2(S_pre / c) (left unset for kScoreScale).
+template <int MODE>
+__device__ __forceinline__ float score_grad(float acc, const ScoreCoef& c, float shift, float* g) {
+  if constexpr (MODE == kScoreScale) {
+    return fmaf(acc, c.k0, -shift);
+  } else if constexpr (MODE == kScoreCapPoly5) {
+    const float a2 = acc * acc;
+    const float q = fmaf(a2, fmaf(a2, c.p5, c.p3), c.p1);
+    *g = fmaf(a2, fmaf(a2, c.g4, c.g2), 1.f);
+    return fmaf(acc, q, -shift);
+  } else {
+    float t2;
+    const float y = score_y<MODE, true>(acc, c, shift, &t2);
+    *g = 1.f - t2;
+    return y;
   }
 }
 

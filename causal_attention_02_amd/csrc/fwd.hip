@@ -407,6 +407,8 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreScale, true>), grid, dim3(256), 0, s, a);
   else if (ss.mode == kScoreScale)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreScale, false>), grid, dim3(256), 0, s, a);
+  else if (ss.mode == kScoreCapPoly5 && ss.fixed_shift)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapPoly5, true>), grid, dim3(256), 0, s, a);
   else if (ss.mode == kScoreCapPoly && ss.fixed_shift)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapPoly, true>), grid, dim3(256), 0, s, a);
   else

@@ -42,9 +42,14 @@ inline ScoreSetup make_score_setup(float scale, float softcap, int D, int qk_nor
     s.mode = kScoreScale;
     s.coef.k0 = (float)(scale * log2e);
   } else if (s.fixed_shift && bound / softcap <= 0.25) {
-    s.mode = kScoreCapPoly;
     // y = c log2e tanh(a scale / c) = a * sum_k t_k (scale/c)^(2k+1) c log2e a^(2k)
     const double x = (double)scale / softcap, k1 = (double)softcap * log2e;
+    const double xm = bound / softcap;  // largest |S_pre / c|
+    // First dropped terms of the degree-5 cut: tanh's x^7 term (in y units) and sech^2's
+    // x^6 term (relative); the series alternate with shrinking terms for |x| < pi/2.
+    const double tail_y = k1 * (17.0 / 315) * pow(xm, 7), tail_g = (17.0 / 45) * pow(xm, 6);
+    const double tol = 1.0 / 4096;
+    s.mode = (tail_y <= tol && tail_g <= tol) ? kScoreCapPoly5 : kScoreCapPoly;
     const double t[5] = {1.0, -1.0 / 3, 2.0 / 15, -17.0 / 315, 62.0 / 2835};
     double pw = x;
     float* p[5] = {&s.coef.p1, &s.coef.p3, &s.coef.p5, &s.coef.p7, &s.coef.p9};
@@ -54,6 +59,8 @@ inline ScoreSetup make_score_setup(float scale, float softcap, int D, int qk_nor
     }
     s.coef.k1 = (float)k1;
     s.coef.inv_k1_sq = (float)(1.0 / (k1 * k1));
+    s.coef.g2 = (float)(-x * x);
+    s.coef.g4 = (float)(2.0 / 3 * x * x * x * x);
   } else {
     s.mode = kScoreCapExp;
     s.coef.k0 = (float)(2.0 * scale * log2e / softcap);
@@ -106,7 +113,8 @@ struct BwdParams {
   const void* o;
   const void* dO;
   const float* lse;  // [B, Hq, T]
-  float* Dvec;       // [B, Hq, T], written by the dq pass
+  float* Dvec;       // [B, Hq, T] -rowsum(dO * O), written by the dq pass
+  float* L2;         // [B, Hq, T] LSE * log2(e), written by the dq pass
   void* dq;
   void* dk;
   void* dv;

@@ -67,10 +67,10 @@ def test_workspace_sizes(L):
     assert L.attn_fwd_workspace_bytes(ctypes.byref(c)) == k_elems * 2
     assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(B=16, T=2048, dtype=bd.ATTN_F32))) == \
         (q_elems + k_elems) * 4
-    assert L.attn_bwd_workspace_bytes(ctypes.byref(c)) == rows * 4 + (q_elems + k_elems) * 2
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(c)) == 2 * rows * 4 + (q_elems + k_elems) * 2
     plain = cfg(B=16, T=2048, opts=bd.AttnOptions())
     assert L.attn_fwd_workspace_bytes(ctypes.byref(plain)) == 0
-    assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == rows * 4
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == 2 * rows * 4
     assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(Hq=5))) == 0  # invalid -> 0
     # Default chunking: 64 x 4 (b, kv head) workgroups already cover the GPU -> one chunk.
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(softcap=50.0, rope=True))

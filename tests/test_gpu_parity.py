@@ -125,6 +125,26 @@ def test_bf16_fwd_bwd_small(w):
     check_bf16(w, got, ref_f, ref_b, w.name, tol_grad=TOL_GRAD if w.T > 2 else 5e-2)
 
 
+def test_softcap_series_degree9():
+    """QK-norm with scale 0.19, D = 128 and cap 100 bounds |S / c| by 0.247: inside the
+    range of the degree-9 tanh series, but the degree-5 cut would move logits by ~4e-4,
+    more than its 2^-12 budget, so this takes the degree-9 score path in every kernel."""
+    import torch
+    w = Workload("poly9", B=1, T=200, Hq=2, Hkv=1, D=128, rope=True, qk_norm=True,
+                 softcap=100.0, seed=11)
+    opts = AttnOptions(softcap=100.0, scale=0.19, rope=True, qk_norm=True)
+    kw = dict(softcap=100.0, scale=0.19, rope=True, qk_norm=True)
+    _say(f"case {w.name}: D=128 scale=0.19 cap=100 norm")
+    q, k, v, dO = make_train_inputs(w)
+    tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+    o, lse = attn_fwd(tq, tk, tv, opts)
+    grads = attn_bwd(tq, tk, tv, o, tdo, lse, opts)
+    torch.cuda.synchronize()
+    got = (to_host(o), to_host(lse)) + tuple(to_host(g) for g in grads)
+    check_bf16(w, got, attention_forward(q, k, v, **kw), attention_backward(q, k, v, dO, **kw),
+               w.name)
+
+
 def test_window_one_identity_on_gpu():
     """W = 1: O = V exactly (P is the identity), dV = dO, dQ = dK = 0."""
     w = Workload("w1", B=1, T=130, Hq=2, Hkv=2, D=64, window=1, rope=True)
