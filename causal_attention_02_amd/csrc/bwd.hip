@@ -97,15 +97,18 @@ __device__ __forceinline__ void finish_grad_row(const f32x16 (&acc)[D / 32], flo
 constexpr int kBMq = 128;  // queries per dq workgroup
 constexpr int kBNk = 64;   // keys per dq tile
 
+// Two waves per SIMD where the registers fit (all D <= 96; D = 128 without a soft-cap).
 template <int D, int MODE>
-__global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = kBNk * CPR / 256;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][kBNk * LD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][kBNk * LD];
+  constexpr int TILE = kBNk * LD;
+  static_assert(kBNk == 64 && TILE % 512 == 0, "tiles are 64 padded rows, whole 1 KB chunks");
+  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
 
   const int T = a.T;
   const int nbh = a.B * a.Hq;
@@ -165,27 +168,11 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
   const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_begin / kBNk, kt1 = (k_end - 1) / kBNk;
 
-  // Rows past T are clamped to row T - 1: finite data that the causal mask removes.
-  uint4 rk[CPT], rv[CPT];
-  auto gload = [&](int kt) {
-    const int k0 = kt * kBNk;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      const int64_t off = (int64_t)min(k0 + row, T - 1) * D + col;
-      rk[c] = ld16<uint4>(kbase + off);
-      rv[c] = ld16<uint4>(vbase + off);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      *reinterpret_cast<uint4*>(&sK[buf][row * LD + col]) = rk[c];
-      *reinterpret_cast<uint4*>(&sV[buf][row * LD + col]) = rv[c];
-    }
+  // Rows past T read clamped, finite data that the causal mask removes.
+  const TileDma<D, 4> tdma(w, l);
+  auto dma = [&](int kt, int buf) {
+    tdma.copy(buf ? sK1 : sK0, kbase, kt * kBNk, T, w);
+    tdma.copy(buf ? sV1 : sV0, vbase, kt * kBNk, T, w);
   };
 
   f32x16 dqacc[NDB];
@@ -199,47 +186,44 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  gload(kt0);
-  sstore(0);
-  __syncthreads();
-  int cur = 0;
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const bool has_next = kt < kt1;
-    if (has_next) gload(kt + 1);
+  // One key tile: S^T = K q^T and dP^T = V dO^T for both 32-key blocks (dP^T accumulates on
+  // top of -D_i, so it comes out as dP - D), then per half block dS and dQ^T += K^T dS^T.
+  // The phase fences keep one phase's registers live at a time (two waves share a SIMD).
+  auto run = [&](int kt, const bf16* sk, const bf16* sv) {
     const int k0 = kt * kBNk;
     const bool skip = !wave_active || k0 > qw_last ||
                       (window > 0 && k0 + kBNk - 1 < qw0 - window + 1);
-    if (!skip) {
-      const bool need_mask = (k0 + kBNk - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
-      const bf16* sk = sK[cur];
-      const bf16* sv = sV[cur];
-      // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
-      const int qd = qi - k0 - 4 * gl;
-      // S^T = K q^T and dP^T = V dO^T for both 32-key blocks are issued first; the VALU work
-      // of block 0 then overlaps block 1's MFMAs and that of block 1 overlaps block 0's dQ.
-      f32x16 sacc[2], pacc[2];
+    if (skip) return;
+    const bool need_mask = (k0 + kBNk - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
+    // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
+    const int qd = qi - k0 - 4 * gl;
+    f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // dP^T accumulates on top of -D_i, so it comes out as dP - D.
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[kb][r] = 0.f;
-          pacc[kb][r] = -Di;
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int off = (kb * 32 + lr) * LD + 16 * s + 8 * gl;
-          const bf16x8 ka = ld16<bf16x8>(sk + off);
-          const bf16x8 va = ld16<bf16x8>(sv + off);
-          sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
-          pacc[kb] = mfma32(va, bdo[s], pacc[kb]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        sacc[kb][r] = 0.f;
+        pacc[kb][r] = -Di;
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int s = 0; s < NS; ++s) {
+        const int off = (kb * 32 + lr) * LD + 16 * s + 8 * gl;
+        const bf16x8 ka = ld16<bf16x8>(sk + off);
+        const bf16x8 va = ld16<bf16x8>(sv + off);
+        sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
+        pacc[kb] = mfma32(va, bdo[s], pacc[kb]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // Half t: elements 8t .. 8t + 7 (keys 16t .. 16t + 15 of the block).
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
         auto grads = [&](auto masked) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * t + e;
             float gf;
             float y = score_grad<MODE>(sacc[kb][r], a.sc, lse2, &gf);
             if constexpr (decltype(masked)::value)
@@ -253,23 +237,36 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
           grads(std::true_type{});
         else
           grads(std::false_type{});
-        const bf16x8 dsb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
+        const bf16x8 dsb = pack8(sacc[kb], 8 * t);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kt_[NDB];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 kt_[NDB];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16* p0 = sk + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-            kt_[db] = tr_read_pair(p0, p0 + 8 * LD);
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(kt_[db], dsb[t], dqacc[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const bf16* p0 = sk + (kb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
+          kt_[db] = tr_read_pair(p0, p0 + 8 * LD);
         }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(kt_[db], dsb, dqacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (has_next) sstore(cur ^ 1);
+  };
+
+  // Two-deep pipeline over key tiles, unrolled by two so each LDS buffer is a distinct
+  // array: the loads into one buffer never wait on reads of the other.
+  dma(kt0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; kt += 2) {
+    if (kt + 1 <= kt1) dma(kt + 1, 1);
+    run(kt, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur ^= 1;
+    if (kt + 1 > kt1) break;
+    if (kt + 2 <= kt1) dma(kt + 2, 0);
+    run(kt + 1, sK1, sV1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   finish_grad_row<D>(dqacc, a.scale, a.q + rowoff, a.dq + rowoff, qrow, gl, a.pro != 0, a.rp,
@@ -281,40 +278,6 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs
 // ------------------------------------------------------------------------------------------
 constexpr int kBNkv = 128;  // keys per dkdv workgroup
 constexpr int kBMt = 64;    // queries per dkdv tile
-
-// Direct global -> LDS copies of 64-row bf16 tiles into LDS rows of pitch D + 8 elements
-// (the pad keeps the row-per-lane MFMA operand reads free of bank conflicts).  The LDS image
-// is cut into 1 KB chunks, one wave-wide 16-byte load each: lane l of chunk c carries image
-// granule p = 64 c + l, which is granule p % G of padded row p / G (G = D/8 + 1).  The
-// source tile is contiguous (rows r0 .. r0 + 63 of one head), so that granule sits
-// p - p / G granules past the tile start; sources are clamped to the head's last granule
-// (rows past the end and the pad granules read real, finite data that is never used).
-// Chunks are dealt round-robin to the NW waves; a wave keeps one offset per chunk it owns.
-template <int D, int NW>
-struct TileDma {
-  static constexpr int G = D / 8 + 1;
-  static constexpr int NC = (G + NW - 1) / NW;  // chunks per wave (the last may be absent)
-  int rel[NC];                                  // granule offset from the tile start
-  __device__ __forceinline__ TileDma(int w, int l) {
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int pg = 64 * (w + NW * i) + l;
-      rel[i] = pg - pg / G;
-    }
-  }
-  // Copy rows r0.. of the head starting at src (T rows) into lds.
-  __device__ __forceinline__ void copy(bf16* lds, const bf16* src, int r0, int T, int w) const {
-    const int first = r0 * (D / 8), last = T * (D / 8) - 1;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = w + NW * i;
-      if (c < G) {
-        const bf16* from = src + 8 * (int64_t)min(first + rel[i], last);
-        __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
-      }
-    }
-  }
-};
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdArgs a) {

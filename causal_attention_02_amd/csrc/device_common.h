@@ -288,4 +288,55 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ---- tile staging ------------------------------------------------------------------------
+// Direct global -> LDS copies of 64-row bf16 tiles into LDS rows of pitch D + 8 elements
+// (the pad keeps the row-per-lane MFMA operand reads free of bank conflicts).  The LDS image
+// is cut into 1 KB chunks, one wave-wide 16-byte load each: lane l of chunk c carries image
+// granule p = 64 c + l, which is granule p % G of padded row p / G (G = D/8 + 1).  The
+// source tile is contiguous (rows r0 .. r0 + 63 of one head), so that granule sits
+// p - p / G granules past the tile start; sources are clamped to the head's last granule
+// (rows past the end and the pad granules read real, finite data that is never used).
+// Chunks are dealt round-robin to the NW waves; a wave keeps one offset per chunk it owns.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int G = D / 8 + 1;
+  static constexpr int NC = (G + NW - 1) / NW;  // chunks per wave (the last may be absent)
+  int rel[NC];                                  // granule offset from the tile start
+  __device__ __forceinline__ TileDma(int w, int l) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int pg = 64 * (w + NW * i) + l;
+      rel[i] = pg - pg / G;
+    }
+  }
+  // Copy rows r0.. of the head starting at src (T rows) into lds.
+  __device__ __forceinline__ void copy(bf16* lds, const bf16* src, int r0, int T, int w) const {
+    const int first = r0 * (D / 8), last = T * (D / 8) - 1;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = w + NW * i;
+      if (c < G) {
+        const bf16* from = src + 8 * (int64_t)min(first + rel[i], last);
+        __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
+      }
+    }
+  }
+  // The same copy with the offsets recomputed in place (three VALU ops per chunk) instead of
+  // held in registers; the empty asm keeps the compiler from hoisting them out of the loop.
+  static __device__ __forceinline__ void copy_fresh(bf16* lds, const bf16* src, int r0, int T,
+                                                    int w, int l) {
+    asm volatile("" : "+v"(l));
+    const int first = r0 * (D / 8), last = T * (D / 8) - 1;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = w + NW * i;
+      if (c < G) {
+        const int pg = 64 * c + l;
+        const bf16* from = src + 8 * (int64_t)min(first + pg - pg / G, last);
+        __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
+      }
+    }
+  }
+};
+
 }  // namespace attn

@@ -63,16 +63,18 @@ __device__ __forceinline__ void pv_block(f32x16 (&oacc)[D / 32], const bf16* sv,
 }
 
 // MODE: score transform (kScore*); FIXED: fixed shift instead of a running maximum.
+// Three waves per SIMD for D <= 96 (registers and 52 KB of LDS per workgroup fit), else two.
 template <int D, int MODE, bool FIXED>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int LD = D + 8;          // LDS row pitch (elements)
   constexpr int NS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int CPT = kBN * CPR / 256;  // chunks per thread per tile
-  static_assert(kBN * CPR % 256 == 0, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][kBN * LD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][kBN * LD];
+  constexpr int TILE = kBN * LD;
+  static_assert(kBN == 64 && TILE % 512 == 0, "tiles are 64 padded rows, whole 1 KB chunks");
+  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
 
   const int T = a.T;
   const int nbh = a.B * a.Hq;
@@ -82,7 +84,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int q0 = qt * kBM, qw0 = q0 + 32 * w;
   const int qi = qw0 + lr;
   const int qrow = min(qi, T - 1);
@@ -116,28 +119,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_begin / kBN, kt1 = (k_end - 1) / kBN;
 
-  // Tile loads: rows past T are clamped to row T - 1 (finite data whose scores the causal
-  // mask removes, since such keys lie after every query).
-  uint4 rk[CPT], rv[CPT];
-  auto gload = [&](int kt) {
-    const int k0 = kt * kBN;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      const int64_t off = (int64_t)min(k0 + row, T - 1) * D + col;
-      rk[c] = ld16<uint4>(kbase + off);
-      rv[c] = ld16<uint4>(vbase + off);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / CPR, col = (idx - row * CPR) * 8;
-      *reinterpret_cast<uint4*>(&sK[buf][row * LD + col]) = rk[c];
-      *reinterpret_cast<uint4*>(&sV[buf][row * LD + col]) = rv[c];
-    }
+  // Tile loads: rows past T read clamped, finite data whose scores the causal mask removes
+  // (such keys lie after every query).
+  auto dma = [&](int kt, int buf) {
+    TileDma<D, 4>::copy_fresh(buf ? sK1 : sK0, kbase, kt * kBN, T, w, l);
+    TileDma<D, 4>::copy_fresh(buf ? sV1 : sV0, vbase, kt * kBN, T, w, l);
   };
 
   float m_run = FIXED ? a.shift : kNegBig, l_run = 0.f;
@@ -152,20 +138,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  gload(kt0);
-  sstore(0);
-  __syncthreads();
-  int cur = 0;
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const bool has_next = kt < kt1;
-    if (has_next) gload(kt + 1);
+  // One key tile against this wave's 32 queries, operands in (sk, sv).
+  auto run = [&](int kt, const bf16* sk, const bf16* sv) {
     const int k0 = kt * kBN;
     const bool skip = !wave_active || k0 > qw_last ||
                       (window > 0 && k0 + kBN - 1 < qw0 - window + 1);
     if (!skip) {
       const bool need_mask = (k0 + kBN - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
-      const bf16* sk = sK[cur];
-      const bf16* sv = sV[cur];
       // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
       const int qd = qi - k0 - 4 * gl;
       if constexpr (FIXED) {
@@ -175,18 +154,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         auto body = [&](auto masked) {
           constexpr bool MASKED = decltype(masked)::value;
           f32x16 sacc[2];
-          bf16x8 ka[2][NS];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-              ka[kb][s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
+            bf16x8 ka[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              ka[s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[kb][s], bq[s], sacc[kb]);
+            for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[s], bq[s], sacc[kb]);
           }
           bf16x8 pb[2][2];
 #pragma unroll
@@ -205,13 +182,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
             l_run += sum_bf16x8(pb[kb][0]) + sum_bf16x8(pb[kb][1]);
             pv_block<D>(oacc, sv, kb, pb[kb], trow, tcol);
           }
-          // Schedule: block 0 scores; block 1 scores under block 0's weights; block 0's PV
-          // under block 1's weights; block 1's PV.
+          // Schedule: block 0 scores; block 1's K reads and score MFMAs under block 0's
+          // weights; block 0's PV under block 1's weights; block 1's PV.
           constexpr int VW = MASKED ? 26 : 22;  // VALU ops per interleave slot
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * NS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, VW, 0);
           }
@@ -275,9 +253,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         }
       }
     }
-    if (has_next) sstore(cur ^ 1);
+  };
+
+  // Two-deep pipeline over key tiles, unrolled by two so each LDS buffer is a distinct
+  // array: the loads into one buffer never wait on reads of the other.
+  dma(kt0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; kt += 2) {
+    if (kt + 1 <= kt1) dma(kt + 1, 1);
+    run(kt, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur ^= 1;
+    if (kt + 1 > kt1) break;
+    if (kt + 2 <= kt1) dma(kt + 2, 0);
+    run(kt + 1, sK1, sV1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   const float l_tot = pair_sum(l_run);
