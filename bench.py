@@ -33,6 +33,38 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal attn fwd+bwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s"
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bwd_dkdv_gqa181m_train.md")
+KERNEL_SOURCES = ["bwd.hip", "device_common.h", "launch.h"]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_attention_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs, calibrated on a plain copy), or None when there is none for this kernel
+    or its sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("bench-traffic:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    break
+            else:
+                return None
+    except OSError:
+        return None
+    if rec.get("kernel") != kernel or rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -47,6 +79,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["train", "decode", "all"], default="all")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (3 times) so HBM byte "
+                         "counters can be calibrated against a known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path has no "
@@ -142,7 +177,7 @@ def main():
         if fam is not None:
             achieved = algo_per_pair[fam] * pairs / (avg_ms * 1e-3) / 1e12
             roof.update(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                        frac=achieved / PEAK_BF16_TFLOPS, traffic=None,
+                        frac=achieved / PEAK_BF16_TFLOPS, traffic=measured_traffic(dom),
                         algorithmic_flops_per_launch=algo_per_pair[fam] * pairs)
         result["roofline"] = roof
         for name in ("flaxchat_full", "flaxchat_w512"):
@@ -153,6 +188,18 @@ def main():
             extra[name] = dict(ms_per_step=ms2, ms_median=float(np.median(per2)), tflops=tf2,
                                pct_peak=100 * tf2 / PEAK_BF16_TFLOPS)
             log(f"[bench] {name}: {ms2:.3f} ms/step  {tf2:.1f} TFLOP/s")
+        torch.cuda.empty_cache()
+
+    if args.copy_mib > 0:
+        nb = args.copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {args.copy_mib} MiB device-to-device")
+        del src, dst
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------------------------
