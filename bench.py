@@ -180,7 +180,8 @@ def main():
                         frac=achieved / PEAK_BF16_TFLOPS, traffic=measured_traffic(dom),
                         algorithmic_flops_per_launch=algo_per_pair[fam] * pairs)
         result["roofline"] = roof
-        for name in ("flaxchat_full", "flaxchat_w512"):
+        for name in ("flaxchat_full", "flaxchat_w512", "gpt_pretrain_train",
+                     "gpt2xl_instruct_train"):
             w = WORKLOADS[name]
             log(f"[bench] fwd+bwd {name}")
             ms2, per2, _ = train_case(w, max(args.steps // 2, 3), 2)
@@ -249,6 +250,30 @@ def main():
                                pct_hbm_peak=100 * gbs / PEAK_HBM_GBS, bytes_per_call=nbytes,
                                kernels_ms=split)
         log(f"[bench] decode: {ms_d * 1e3:.1f} us/call  {gbs:.0f} GB/s")
+        # The GPT pretraining page's KV-cache shape (one sequence, 256 cached rows, 12 heads,
+        # d 64): latency-bound, reported per call.
+        ws = WORKLOADS["gpt_pretrain_decode"]
+        qs, kcs, vcs, lens_s = make_decode_inputs(ws)
+        tqs, tks, tvs = to_dev(qs), to_dev(kcs), to_dev(vcs)
+        tls = torch.from_numpy(lens_s).to(dev)
+        os_ = torch.empty_like(tqs)
+        opts_s = opts_of(ws)
+        cfg_s = bd.make_decode_cfg(ws.B, ws.Hq, ws.Hkv, ws.D, ws.T, opts_s)
+        wss = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg_s))),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(10):
+            bd.attn_decode(tqs, tks, tvs, tls, opts_s, out=os_, workspace=wss)
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evs[0].record(stream)
+        for _ in range(n):
+            bd.attn_decode(tqs, tks, tvs, tls, opts_s, out=os_, workspace=wss)
+        evs[1].record(stream)
+        torch.cuda.synchronize()
+        us_s = evs[0].elapsed_time(evs[1]) / n * 1e3
+        extra["gpt_pretrain_decode"] = dict(us_per_call=us_s,
+                                            GBps=decode_bytes(ws, lens_s) / (us_s * 1e-6) / 1e9)
+        log(f"[bench] gpt_pretrain_decode: {us_s:.1f} us/call")
         if "value" not in result:
             result.update(value=gbs, ms_per_step=ms_d)
 

@@ -80,6 +80,16 @@ WORKLOADS = {
     "gqa181m_decode": Workload("gqa181m_decode", B=64, T=2048, Hq=8, Hkv=4, D=96, softcap=50.0,
                                rope=True, backward=False, decode=True, len_lo=256,
                                seed=SEED_BASE + 4),
+    # GPT pretraining page: 768 dims over 12 heads -> d = 64, context 256, batch 128; plain
+    # causal multi-head attention (learned position embeddings, no RoPE / QK-norm / cap).
+    "gpt_pretrain_train": Workload("gpt_pretrain_train", B=128, T=256, Hq=12, Hkv=12, D=64,
+                                   seed=SEED_BASE + 5),
+    # Instruction tuning on GPT-2 XL: 1600 dims over 25 heads -> d = 64, context 256, batch 8.
+    "gpt2xl_instruct_train": Workload("gpt2xl_instruct_train", B=8, T=256, Hq=25, Hkv=25, D=64,
+                                      seed=SEED_BASE + 6),
+    # The GPT pretraining page's KV-cache run: one sequence, full 256-token context, 12 heads.
+    "gpt_pretrain_decode": Workload("gpt_pretrain_decode", B=1, T=256, Hq=12, Hkv=12, D=64,
+                                    backward=False, decode=True, len_lo=256, seed=SEED_BASE + 7),
 }
 
 

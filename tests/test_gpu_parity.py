@@ -159,7 +159,8 @@ def test_window_one_identity_on_gpu():
 # --------------------------------------------------------------------------------------------
 # Full-size workloads, sampled (b, kv-group) slices
 # --------------------------------------------------------------------------------------------
-FULL = ["gqa181m_train", "flaxchat_full", "flaxchat_w512"]
+FULL = ["gqa181m_train", "flaxchat_full", "flaxchat_w512", "gpt_pretrain_train",
+        "gpt2xl_instruct_train"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -169,7 +170,7 @@ def test_full_size_sampled(name):
     q, k, v, dO = make_train_inputs(w)
     got = gpu_fwd_bwd(w, q, k, v, dO)
     G = w.Hq // w.Hkv
-    for b, g in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+    for b, g in [(0, 0), (w.B // 2, w.Hkv // 2), (w.B - 1, w.Hkv - 1)]:
         hs = slice(g * G, (g + 1) * G)
         qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
         ref_f = attention_forward(qs, ks, vs, **oracle_kw(w))
@@ -206,8 +207,9 @@ def gpu_decode(w, q, kc, vc, lens, split_len=0):
     return to_host(o)
 
 
-def test_decode_full_size():
-    w = WORKLOADS["gqa181m_decode"]
+@pytest.mark.parametrize("name", ["gqa181m_decode", "gpt_pretrain_decode"])
+def test_decode_full_size(name):
+    w = WORKLOADS[name]
     _say(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} Lmax={w.T}")
     q, kc, vc, lens = make_decode_inputs(w)
     o = gpu_decode(w, q, kc, vc, lens)

@@ -379,3 +379,16 @@ def test_workload_shapes_match_pages():
     for name in ("flaxchat_full", "flaxchat_w512"):
         w = WORKLOADS[name]
         assert (w.Hq, w.Hkv, w.D) == (fc["heads"], fc["kv_heads"], fc["model_dim"] // fc["heads"])
+    gp, g2 = ps["gpt_pretrain"], ps["gpt2_family"]
+    w = WORKLOADS["gpt_pretrain_train"]
+    assert (w.B, w.T, w.Hq, w.Hkv, w.D) == (gp["batch_size"], gp["context_length"], gp["num_heads"],
+                                            gp["num_heads"], gp["d_model"] // gp["num_heads"])
+    w = WORKLOADS["gpt_pretrain_decode"]
+    demo = gp["kv_cache_demo"]
+    assert (w.B, w.T, w.len_lo, w.Hq, w.D) == (demo["batch"], demo["context_length"],
+                                               demo["context_length"], gp["num_heads"], 64)
+    w = WORKLOADS["gpt2xl_instruct_train"]
+    d_model, heads = g2["sizes"][-1]
+    assert (w.B, w.T, w.Hq, w.Hkv, w.D) == (g2["batch_size"], g2["context_length"], heads, heads,
+                                            d_model // heads)
+    assert all(dm // h == 64 for dm, h in g2["sizes"])
