@@ -2,6 +2,7 @@
 from .attn_ref import (  # noqa: F401
     attention_backward,
     attention_decode,
+    attention_extend,
     attention_forward,
     rms_normalize,
     rope_rotate,

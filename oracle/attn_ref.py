@@ -23,7 +23,9 @@ What it computes (sources, by page title and section):
   "Core Features".
 * KV-cache decode: one new query attends over every cached key; with
   offset = k_len - q_len, query i may see key j iff j <= offset + i -- "GPT
-  pretraining" page, section "Bonus: KV Caching".
+  pretraining" page, section "Bonus: KV Caching".  The same section's step (compute
+  the new tokens' keys and values, append them to the cache, attend over the whole
+  history) with more than one new token is ``attention_extend``.
 
 Readings of what the pages leave open (each also listed with its reason in the
 project's design notes):
@@ -38,6 +40,10 @@ project's design notes):
 * Decode: the cache already holds the new token's (rotated) key/value, so the query
   sits at position L_b - 1 and sees all L_b cached keys; a sequence with L_b = 0
   yields an all-zero output row.
+* Extend: cache_len counts the rows present before the step; new token i sits at
+  position L_b + i, its key is rotated at that position (and normalised) before it
+  is stored, and rows that would land at or past Lmax are not stored (their queries
+  return zero rows).
 
 Everything is computed densely per (batch, head) in float64 with numpy; there is
 no tiling, fusion or reordering beyond the definitions above.
@@ -54,6 +60,7 @@ __all__ = [
     "attention_forward",
     "attention_backward",
     "attention_decode",
+    "attention_extend",
 ]
 
 
@@ -281,3 +288,57 @@ def attention_decode(q, k_cache, v_cache, cache_len, *, softcap=0.0, scale=None,
             P, _ = _softmax_rows(s, np.ones_like(s, dtype=bool))
             o[b, h] = (P @ vc[b, g, :L])[0]
     return o
+
+
+def attention_extend(q, k_new, v_new, k_cache, v_cache, cache_len, *, window=0, softcap=0.0,
+                     scale=None, rope=False, rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+    """S new tokens per sequence against a KV cache ("GPT pretraining" page, "Bonus: KV Caching").
+
+    q [B,Hq,S,d], k_new/v_new [B,Hkv,S,d] are raw (before RoPE / QK-norm); the caches
+    [B,Hkv,Lmax,d] hold rotated (and normalised) keys in rows < cache_len[b].  Token i of
+    sequence b sits at position p = L_b + i: its key (rotated at p, normalised) and value are
+    stored in row p, and its query (rotated at p, normalised) attends over keys j <= p (and
+    j > p - window with a window) -- the page's offset rule with offset = L_b.
+    cache_len is clamped to [0, Lmax]; tokens with p >= Lmax are not stored and give zero
+    output rows.  Returns (o [B,Hq,S,d], k_cache', v_cache'); the inputs are not modified.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kn = np.asarray(k_new, dtype=np.float64)
+    vn = np.asarray(v_new, dtype=np.float64)
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    if q.ndim != 4 or kn.ndim != 4 or kn.shape != vn.shape:
+        raise ValueError("q must be [B,Hq,S,d] and k_new/v_new [B,Hkv,S,d]")
+    B, Hq, S, d = q.shape
+    if kn.shape[0] != B or kn.shape[2] != S or kn.shape[3] != d:
+        raise ValueError("k_new/v_new must match q in B, S and d")
+    if kc.ndim != 4 or kc.shape != vc.shape or kc.shape[0] != B or kc.shape[1] != kn.shape[1] \
+            or kc.shape[3] != d:
+        raise ValueError("caches must be [B, Hkv, Lmax, d] matching k_new")
+    Hkv, Lmax = kc.shape[1], kc.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(d)
+    group = Hq // Hkv
+    o = np.zeros((B, Hq, S, d))
+    for b in range(B):
+        L = int(min(max(int(cache_len[b]), 0), Lmax))
+        n = min(S, Lmax - L)  # tokens that fit in the cache
+        if n <= 0:
+            continue
+        pos = L + np.arange(n)
+        khat, _ = _prologue(kn[b][:, :n], pos, rope, rope_base, qk_norm, norm_eps)
+        kc[b, :, L:L + n] = khat
+        vc[b, :, L:L + n] = vn[b][:, :n]
+        qhat, _ = _prologue(q[b][:, :n], pos, rope, rope_base, qk_norm, norm_eps)
+        j = np.arange(L + n)[None, :]
+        allowed = j <= pos[:, None]
+        if window > 0:
+            allowed &= (pos[:, None] - j) < window
+        for h in range(Hq):
+            g = h // group
+            _, sc = _scores(qhat[h], kc[b, g, :L + n], scale, softcap)
+            P, _ = _softmax_rows(sc, allowed)
+            o[b, h, :n] = P @ vc[b, g, :L + n]
+    return o, kc, vc

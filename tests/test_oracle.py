@@ -14,8 +14,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_backward, attention_decode, attention_forward, rms_normalize,
-                    rope_rotate, rope_unrotate, visible_mask)
+from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
+                    rms_normalize, rope_rotate, rope_unrotate, visible_mask)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -359,6 +359,134 @@ def test_decode_zero_length_and_clamp():
     np.testing.assert_array_equal(o[1], 0.0)
     o_full = attention_decode(q[2:], kc[2:], vc[2:], np.array([6]))
     np.testing.assert_allclose(o[2], o_full[0], atol=0)
+
+
+# ------------------------------------------------------------------------------------
+# Extend: S new tokens against a KV cache (append, then attend with the offset mask).
+# ------------------------------------------------------------------------------------
+def brute_force_extend(q, kn, vn, kc, vc, lens, window, softcap, rope, qk_norm, base=10000.0,
+                       eps=1e-6):
+    B, Hq, S, d = q.shape
+    Hkv, Lmax = kc.shape[1], kc.shape[2]
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, S, d))
+    K, V = kc.copy(), vc.copy()
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), Lmax)
+        for g, i in itertools.product(range(Hkv), range(S)):
+            if L + i < Lmax:
+                K[b, g, L + i] = _bf_prologue(kn[b, g, i], L + i, rope, base, qk_norm, eps)
+                V[b, g, L + i] = vn[b, g, i]
+        for h, i in itertools.product(range(Hq), range(S)):
+            p = L + i
+            if p >= Lmax:
+                continue
+            g = h * Hkv // Hq
+            qi = _bf_prologue(q[b, h, i], p, rope, base, qk_norm, eps)
+            keys = [j for j in range(p + 1) if window == 0 or p - j < window]
+            sc = []
+            for j in keys:
+                s_ = scale * sum(a * c for a, c in zip(qi, K[b, g, j]))
+                sc.append(softcap * math.tanh(s_ / softcap) if softcap else s_)
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            for jj, j in enumerate(keys):
+                O[b, h, i] += w[jj] / sum(w) * V[b, g, j]
+    return O, K, V
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_extend_matches_brute_force(flags):
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, S, d, Lmax = 3, 4, 2, 3, 6, 8
+    q, kn, vn = rnd(rng, B, Hq, S, d), rnd(rng, B, Hkv, S, d), rnd(rng, B, Hkv, S, d)
+    kc, vc = rnd(rng, B, Hkv, Lmax, d), rnd(rng, B, Hkv, Lmax, d)
+    lens = np.array([2, 0, 6])  # the last sequence overflows: only 2 of its 3 tokens fit
+    O, K, V = attention_extend(q, kn, vn, kc, vc, lens, **flags)
+    Ob, Kb, Vb = brute_force_extend(q, kn, vn, kc, vc, lens, **flags)
+    np.testing.assert_allclose(O, Ob, atol=1e-12)
+    np.testing.assert_allclose(K, Kb, atol=1e-12)
+    np.testing.assert_allclose(V, Vb, atol=0)
+    np.testing.assert_array_equal(O[2, :, 2], 0.0)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_extend_on_empty_cache_is_the_forward(flags):
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, T, d = 2, 4, 2, 9, 8
+    q, k, v = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d)
+    kc, vc = rnd(rng, B, Hkv, T + 3, d), rnd(rng, B, Hkv, T + 3, d)
+    O, K, V = attention_extend(q, k, v, kc, vc, np.zeros(B, int), **flags)
+    Of, _ = attention_forward(q, k, v, **flags)
+    np.testing.assert_allclose(O, Of, atol=1e-13)
+    kr = rope_rotate(k, np.arange(T)) if flags["rope"] else k
+    kr = rms_normalize(kr)[0] if flags["qk_norm"] else kr
+    np.testing.assert_allclose(K[:, :, :T], kr, atol=1e-14)
+    np.testing.assert_array_equal(V[:, :, :T], v)
+    np.testing.assert_array_equal(K[:, :, T:], kc[:, :, T:])  # rows past the new ones untouched
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS[:3])
+def test_extend_one_token_is_decode(flags):
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, d, Lmax = 3, 4, 2, 8, 12
+    q, kn, vn = rnd(rng, B, Hq, 1, d), rnd(rng, B, Hkv, 1, d), rnd(rng, B, Hkv, 1, d)
+    kc, vc = rnd(rng, B, Hkv, Lmax, d), rnd(rng, B, Hkv, Lmax, d)
+    lens = np.array([0, 5, 11])
+    O, K, V = attention_extend(q, kn, vn, kc, vc, lens, **flags)
+    dec = attention_decode(q[:, :, 0], K, V, lens + 1,
+                           **{a: b for a, b in flags.items() if a != "window"})
+    np.testing.assert_allclose(O[:, :, 0], dec, atol=1e-13)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_extend_chunks_compose(flags):
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, S1, S2, d, Lmax = 2, 2, 1, 3, 4, 8, 16
+    q, kn, vn = rnd(rng, B, Hq, S1 + S2, d), rnd(rng, B, Hkv, S1 + S2, d), rnd(rng, B, Hkv, S1 + S2, d)
+    kc, vc = rnd(rng, B, Hkv, Lmax, d), rnd(rng, B, Hkv, Lmax, d)
+    lens = np.array([4, 1])
+    O, K, V = attention_extend(q, kn, vn, kc, vc, lens, **flags)
+    O1, K1, V1 = attention_extend(q[:, :, :S1], kn[:, :, :S1], vn[:, :, :S1], kc, vc, lens, **flags)
+    O2, K2, V2 = attention_extend(q[:, :, S1:], kn[:, :, S1:], vn[:, :, S1:], K1, V1, lens + S1,
+                                  **flags)
+    np.testing.assert_allclose(O, np.concatenate([O1, O2], axis=2), atol=1e-13)
+    np.testing.assert_allclose(K, K2, atol=0)
+    np.testing.assert_allclose(V, V2, atol=0)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_extend_is_the_forward_suffix(flags):
+    """A cache filled with the first L prepared keys, then S more tokens: the outputs are the
+    last S rows of the forward over the whole sequence."""
+    rng = np.random.default_rng(25)
+    B, Hq, Hkv, T, d = 3, 4, 2, 11, 8
+    q, k, v = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d)
+    Of, _ = attention_forward(q, k, v, **flags)
+    kr = rope_rotate(k, np.arange(T)) if flags["rope"] else k
+    kr = rms_normalize(kr)[0] if flags["qk_norm"] else kr
+    for L in (0, 4, T - 1):
+        kc = np.full((B, Hkv, T, d), np.nan)
+        vc = np.full((B, Hkv, T, d), np.nan)
+        kc[:, :, :L], vc[:, :, :L] = kr[:, :, :L], v[:, :, :L]
+        O, K, V = attention_extend(q[:, :, L:], k[:, :, L:], v[:, :, L:], kc, vc,
+                                   np.full(B, L), **flags)
+        np.testing.assert_allclose(O, Of[:, :, L:], atol=1e-13)
+        np.testing.assert_allclose(K, kr, atol=1e-14)
+
+
+def test_extend_clamps_and_leaves_inputs():
+    rng = np.random.default_rng(26)
+    q, kn, vn = rnd(rng, 2, 2, 3, 4), rnd(rng, 2, 1, 3, 4), rnd(rng, 2, 1, 3, 4)
+    kc, vc = rnd(rng, 2, 1, 5, 4), rnd(rng, 2, 1, 5, 4)
+    kc0, vc0 = kc.copy(), vc.copy()
+    O, K, V = attention_extend(q, kn, vn, kc, vc, np.array([-4, 99]))
+    np.testing.assert_array_equal(kc, kc0)
+    np.testing.assert_array_equal(vc, vc0)
+    Oz, _, _ = attention_extend(q[:1], kn[:1], vn[:1], kc[:1], vc[:1], np.array([0]))
+    np.testing.assert_allclose(O[0], Oz[0], atol=0)  # negative length counts as 0
+    np.testing.assert_array_equal(O[1], 0.0)  # a full cache stores nothing and attends nothing
+    np.testing.assert_array_equal(K[1], kc[1])
 
 
 # ------------------------------------------------------------------------------------
