@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     AttnOptions,
     attn_bwd,
     attn_decode,
+    attn_extend,
     attn_fwd,
     bwd_workspace_bytes,
     fwd_workspace_bytes,

@@ -19,8 +19,8 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = [
     "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes",
-    "attn_check_cfg", "attn_check_decode_cfg", "attn_fwd", "attn_bwd", "attn_decode",
-    "attn_status_str", "attn_trace_enable", "attn_trace_read",
+    "attn_check_cfg", "attn_check_decode_cfg", "attn_check_extend_cfg", "attn_fwd", "attn_bwd",
+    "attn_decode", "attn_extend", "attn_status_str", "attn_trace_enable", "attn_trace_read",
 ]
 
 
@@ -38,6 +38,14 @@ class AttnDecodeCfg(ctypes.Structure):
                 ("scale", ctypes.c_float), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
                 ("qk_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float),
                 ("split_len", ctypes.c_int32)]
+
+
+class AttnExtendCfg(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("Lmax", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("scale", ctypes.c_float), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("qk_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
 
 
 class AttnTraceEntry(ctypes.Structure):
@@ -64,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         cfgp, dcfgp = ctypes.POINTER(AttnCfg), ctypes.POINTER(AttnDecodeCfg)
+        ecfgp = ctypes.POINTER(AttnExtendCfg)
         L.attn_fwd_workspace_bytes.argtypes = [cfgp]
         L.attn_fwd_workspace_bytes.restype = sz
         L.attn_bwd_workspace_bytes.argtypes = [cfgp]
@@ -74,12 +83,16 @@ def lib() -> ctypes.CDLL:
         L.attn_check_cfg.restype = ctypes.c_int
         L.attn_check_decode_cfg.argtypes = [dcfgp]
         L.attn_check_decode_cfg.restype = ctypes.c_int
+        L.attn_check_extend_cfg.argtypes = [ecfgp]
+        L.attn_check_extend_cfg.restype = ctypes.c_int
         L.attn_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_fwd.restype = ctypes.c_int
         L.attn_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_bwd.restype = ctypes.c_int
         L.attn_decode.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_decode.restype = ctypes.c_int
+        L.attn_extend.argtypes = [ecfgp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_extend.restype = ctypes.c_int
         L.attn_status_str.argtypes = [ctypes.c_int]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_trace_enable.argtypes = [ctypes.c_int]
@@ -121,6 +134,12 @@ def make_decode_cfg(B, Hq, Hkv, D, Lmax, opts: AttnOptions, split_len: int = 0) 
     return AttnDecodeCfg(B, Hq, Hkv, D, Lmax, float(opts.softcap), float(opts.scale),
                          int(bool(opts.rope)), float(opts.rope_base), int(bool(opts.qk_norm)),
                          float(opts.norm_eps), int(split_len))
+
+
+def make_extend_cfg(B, S, Hq, Hkv, D, Lmax, opts: AttnOptions) -> AttnExtendCfg:
+    return AttnExtendCfg(B, S, Hq, Hkv, D, Lmax, int(opts.window), float(opts.softcap),
+                         float(opts.scale), int(bool(opts.rope)), float(opts.rope_base),
+                         int(bool(opts.qk_norm)), float(opts.norm_eps))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -255,6 +274,31 @@ def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None,
                            ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
                            _stream(stream))
     _check(st, "attn_decode")
+    return o
+
+
+def attn_extend(q, k_new, v_new, k_cache, v_cache, cache_len, opts: AttnOptions | None = None, *,
+                out=None, stream=None):
+    """S new tokens against a KV cache (bf16): q [B,Hq,S,D], k_new/v_new [B,Hkv,S,D], caches
+    [B,Hkv,Lmax,D] (rows cache_len[b] .. cache_len[b]+S-1 are written), cache_len int32 [B]
+    (not modified) -> o [B,Hq,S,D]."""
+    torch = _torch()
+    opts = opts or AttnOptions()
+    B, Hq, S, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    bf = torch.bfloat16
+    _need(q, (B, Hq, S, D), bf, "q")
+    _need(k_new, (B, Hkv, S, D), bf, "k_new")
+    _need(v_new, (B, Hkv, S, D), bf, "v_new")
+    _need(k_cache, (B, Hkv, Lmax, D), bf, "k_cache")
+    _need(v_cache, (B, Hkv, Lmax, D), bf, "v_cache")
+    _need(cache_len, (B,), torch.int32, "cache_len")
+    o = torch.empty_like(q) if out is None else out
+    _need(o, q.shape, bf, "out")
+    cfg = make_extend_cfg(B, S, Hq, Hkv, D, Lmax, opts)
+    st = lib().attn_extend(ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                           _ptr(v_cache), _ptr(cache_len), _ptr(o), _stream(stream))
+    _check(st, "attn_extend")
     return o
 
 

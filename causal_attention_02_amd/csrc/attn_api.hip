@@ -107,6 +107,25 @@ int check_dcfg(const attn_decode_cfg* c) {
   return ATTN_OK;
 }
 
+int check_ecfg(const attn_extend_cfg* c) {
+  if (!c) return ATTN_EINVAL;
+  if (c->B < 0 || c->S < 0 || c->Lmax < 0 || c->window < 0) return ATTN_EINVAL;
+  if (c->Hq < 1 || c->Hkv < 1 || c->Hq % c->Hkv != 0) return ATTN_EINVAL;
+  if (!(c->softcap >= 0.f) || !isfinite(c->softcap)) return ATTN_EINVAL;
+  if (!(c->scale >= 0.f) || !isfinite(c->scale)) return ATTN_EINVAL;
+  if (c->rope != 0 && c->rope != 1) return ATTN_EINVAL;
+  if (c->rope && (!(c->rope_base > 0.f) || !isfinite(c->rope_base))) return ATTN_EINVAL;
+  if (c->qk_norm != 0 && c->qk_norm != 1) return ATTN_EINVAL;
+  if (c->qk_norm && (!(c->norm_eps > 0.f) || !isfinite(c->norm_eps))) return ATTN_EINVAL;
+  if (c->D <= 0) return ATTN_EINVAL;
+  if (!supported_d(c->D)) return ATTN_EUNSUPPORTED;
+  if ((int64_t)c->Lmax * c->D > INT32_MAX || (int64_t)c->S * c->D > INT32_MAX)
+    return ATTN_EUNSUPPORTED;
+  // Forward grid: one workgroup per (128 new tokens, b, query head).
+  if ((int64_t)((c->S + 127) / 128) * c->B * c->Hq > INT32_MAX) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
 float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
 
 // Default chunking: enough (b, kv head, head subset, chunk) workgroups to cover about 256
@@ -171,6 +190,7 @@ const char* attn_status_str(int s) {
 
 int attn_check_cfg(const attn_cfg* cfg, int for_backward) { return check_cfg(cfg, for_backward); }
 int attn_check_decode_cfg(const attn_decode_cfg* cfg) { return check_dcfg(cfg); }
+int attn_check_extend_cfg(const attn_extend_cfg* cfg) { return check_ecfg(cfg); }
 
 size_t attn_fwd_workspace_bytes(const attn_cfg* cfg) {
   return check_cfg(cfg, 0) == ATTN_OK ? fwd_ws(cfg) : 0;
@@ -270,6 +290,29 @@ int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, co
                  c->Lmax, decode_split_len(c), decode_nsplit(c), eff_scale(c->scale, c->D),
                  c->softcap, c->rope, c->rope_base, c->qk_norm, c->norm_eps};
   return launch_status(launch_decode(p, (hipStream_t)stream));
+}
+
+int attn_extend(const attn_extend_cfg* c, const void* q, const void* k_new, const void* v_new,
+                void* k_cache, void* v_cache, const int32_t* cache_len, void* o, void* stream) {
+  int st = check_ecfg(c);
+  if (st != ATTN_OK) return st;
+  if (c->B == 0 || c->S == 0) return ATTN_OK;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !o) return ATTN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  // 1. Store the new tokens' keys (RoPE at their positions, QK-norm) and values.
+  hipError_t e = launch_append_kv(k_new, v_new, k_cache, v_cache, cache_len, c->B, c->Hkv, c->S,
+                                  c->Lmax, c->D, c->rope, c->rope_base, c->qk_norm, c->norm_eps,
+                                  s);
+  // 2. The forward kernel in cache mode: queries at positions cache_len[b] + i over the cache.
+  if (e == hipSuccess) {
+    FwdParams p{q, k_cache, v_cache, o, nullptr, c->B, c->S, c->Hq, c->Hkv, c->D, c->window,
+                eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
+                c->norm_eps};
+    p.cache_len = cache_len;
+    p.Lmax = c->Lmax;
+    e = launch_fwd_bf16(p, s);
+  }
+  return launch_status(e);
 }
 
 int attn_trace_enable(int on) {

@@ -32,8 +32,10 @@ struct FwdArgs {
   const bf16* k;
   const bf16* v;
   bf16* o;
-  float* lse;
+  float* lse;                // may be null (extend: no LSE output)
+  const int32_t* cache_len;  // extend: rows already cached per sequence (null in training)
   int B, T, Hq, Hkv, window, nqt;
+  int Tk;                    // rows per head of k/v (T in training, Lmax for a cache)
   float shift;  // fixed softmax shift (log2 units) when the score bound allows one
   ScoreCoef sc;
   RowPrologue rp;
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
 
-  const int T = a.T;
+  const int T = a.T;  // query rows per head
   const int nbh = a.B * a.Hq;
   const int rank = blockIdx.x / nbh;  // heaviest (last) query tiles first
   const int bh = blockIdx.x - rank * nbh;
@@ -88,12 +90,26 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int q0 = qt * kBM, qw0 = q0 + 32 * w;
   const int qi = qw0 + lr;
-  const int qrow = min(qi, T - 1);
+  // Extend (a KV cache): query i sits at position off + i and the cache holds off + nq keys
+  // after the append; queries that did not fit (off + i >= Lmax) get zero rows.  Training:
+  // off = 0 and nq = nk = T.
+  const int Tk = a.Tk;
+  const int off = a.cache_len ? min(max(a.cache_len[b], 0), Tk) : 0;
+  const int nq = min(T, Tk - off);
+  const int nk = off + nq;
+  if (q0 >= nq) {
+    for (int t = tid; t < kBM * D; t += 256) {
+      const int r = q0 + t / D;
+      if (r < T) a.o[((int64_t)bh * T + r) * D + t % D] = to_bf16(0.f);
+    }
+    return;
+  }
+  const int qrow = min(qi, nq - 1);
   const int window = a.window;
   const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
 
-  const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * T * D;
-  const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
+  const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * Tk * D;
+  const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * Tk * D;
 
   // Q operand: lane holds q^[qi][16 s + 8 gl .. +7]; RoPE and RMSNorm are applied here.
   bf16x8 bq[NS];
@@ -107,7 +123,7 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int p = 0; p < 8; ++p) x[s][p] = (float)bq[s][p];
-      prologue_oplayout<NS>(x, qrow, gl, a.rp, D);
+      prologue_oplayout<NS>(x, off + qrow, gl, a.rp, D);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -115,15 +131,15 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
     }
   }
 
-  const int k_end = min(T, q0 + kBM);
-  const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
+  const int k_end = min(nk, off + q0 + kBM);
+  const int k_begin = window > 0 ? max(0, off + q0 - window + 1) : 0;
   const int kt0 = k_begin / kBN, kt1 = (k_end - 1) / kBN;
 
   // Tile loads: rows past T read clamped, finite data whose scores the causal mask removes
   // (such keys lie after every query).
   auto dma = [&](int kt, int buf) {
-    TileDma<D, 4>::copy_fresh(buf ? sK1 : sK0, kbase, kt * kBN, T, w, l);
-    TileDma<D, 4>::copy_fresh(buf ? sV1 : sV0, vbase, kt * kBN, T, w, l);
+    TileDma<D, 4>::copy_fresh(buf ? sK1 : sK0, kbase, kt * kBN, nk, w, l);
+    TileDma<D, 4>::copy_fresh(buf ? sV1 : sV0, vbase, kt * kBN, nk, w, l);
   };
 
   float m_run = FIXED ? a.shift : kNegBig, l_run = 0.f;
@@ -133,20 +149,21 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  const bool wave_active = qw0 < T;
-  const int qw_last = min(qw0 + 31, T - 1);
+  // Positions of the wave's first and last existing query.
+  const bool wave_active = qw0 < nq;
+  const int pw0 = off + qw0, pw_last = off + min(qw0 + 31, nq - 1);
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
   // One key tile against this wave's 32 queries, operands in (sk, sv).
   auto run = [&](int kt, const bf16* sk, const bf16* sv) {
     const int k0 = kt * kBN;
-    const bool skip = !wave_active || k0 > qw_last ||
-                      (window > 0 && k0 + kBN - 1 < qw0 - window + 1);
+    const bool skip = !wave_active || k0 > pw_last ||
+                      (window > 0 && k0 + kBN - 1 < pw0 - window + 1);
     if (!skip) {
-      const bool need_mask = (k0 + kBN - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
-      // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
-      const int qd = qi - k0 - 4 * gl;
+      const bool need_mask = (k0 + kBN - 1 > pw0) || (window > 0 && k0 < pw_last - window + 1);
+      // position - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
+      const int qd = off + qi - k0 - 4 * gl;
       if constexpr (FIXED) {
         // One straight-line body per mask variant, software-pipelined over the two 32-key
         // blocks: block 1's score MFMAs are interleaved with block 0's weight VALU work, and
@@ -273,7 +290,7 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   }
 
   const float l_tot = pair_sum(l_run);
-  if (qi < T) {
+  if (qi < nq) {
     const float inv = 1.f / l_tot;
     bf16* op = a.o + ((int64_t)bh * T + qi) * D;
 #pragma unroll
@@ -285,7 +302,18 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
         for (int j = 0; j < 4; ++j) v4[j] = to_bf16(oacc[db][4 * i4 + j] * inv);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i4 + 4 * gl) = v4;
       }
-    if (gl == 0) a.lse[(int64_t)bh * T + qi] = (m_run + log2_fast(l_tot)) * kLn2;
+    if (gl == 0 && a.lse) a.lse[(int64_t)bh * T + qi] = (m_run + log2_fast(l_tot)) * kLn2;
+  } else if (qi < T) {
+    bf16* op = a.o + ((int64_t)bh * T + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 z;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] = to_bf16(0.f);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i4 + 4 * gl) = z;
+      }
   }
 }
 
@@ -382,8 +410,10 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   a.v = (const bf16*)p.v;
   a.o = (bf16*)p.o;
   a.lse = p.lse;
+  a.cache_len = p.cache_len;
   a.B = p.B;
   a.T = p.T;
+  a.Tk = p.cache_len ? p.Lmax : p.T;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.window = p.window;

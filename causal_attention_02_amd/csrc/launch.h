@@ -83,6 +83,11 @@ inline RowPrologue make_row_prologue(int rope, float rope_base, int qk_norm, flo
 
 // ---- row passes (rowops.hip) -------------------------------------------------------------
 // y = N(R(x)) for rows of length D; row r sits at position r % T.  elt = 2 (bf16) or 4 (f32).
+// k_new/v_new [B, Hkv, S, D] -> cache rows cache_len[b] + i (RoPE at that position, QK-norm);
+// rows at or past Lmax are not written.
+hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
+                            const int32_t* cache_len, int B, int Hkv, int S, int Lmax, int D,
+                            int rope, float rope_base, int qk_norm, float eps, hipStream_t s);
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s);
 
@@ -99,6 +104,10 @@ struct FwdParams {
   float rope_base;
   int qk_norm;
   float eps;
+  // Extend mode: q holds T new tokens per sequence, k/v are caches of Lmax rows per head
+  // (already holding the new keys), query i sits at position cache_len[b] + i.
+  const int32_t* cache_len = nullptr;
+  int Lmax = 0;
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);  // q, k already prologued

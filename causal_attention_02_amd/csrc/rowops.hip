@@ -112,6 +112,87 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(const bf16* __restri
   }
 }
 
+// Append S new tokens to a KV cache ("GPT pretraining" page, "Bonus: KV Caching": compute
+// the new keys and values, append them, then attend).  Token i of sequence b lands in cache
+// row p = cache_len[b] + i (cache_len clamped to [0, Lmax]); its key is rotated at p and
+// normalised first, its value copied.  Rows with p >= Lmax are not written.  Same lane layout
+// as prologue_bf16_kernel: 8 lanes per row, each owning 8 RoPE pairs.
+__global__ __launch_bounds__(256) void append_kv_kernel(const bf16* __restrict__ kn,
+                                                        const bf16* __restrict__ vn,
+                                                        bf16* __restrict__ kc, bf16* __restrict__ vc,
+                                                        const int32_t* __restrict__ cache_len,
+                                                        int64_t rows, int S, int Hkv, int Lmax, int D,
+                                                        RowPrologue rp) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);  // (b, g, i) row-major
+  const int u = threadIdx.x & 7;
+  const bool in_range = row < rows;
+  const int64_t bg = in_range ? row / S : 0;
+  const int i = in_range ? (int)(row - bg * S) : 0;
+  const int b = (int)(bg / Hkv);
+  const int L = in_range ? min(max(cache_len[b], 0), Lmax) : 0;
+  const int pos = L + i;
+  const bool act = in_range && pos < Lmax && u < D / 16;
+  const int half = D / 2;
+  float x1[8], x2[8];
+  const bf16* xr = kn + (in_range ? row : 0) * D;
+  if (act) {
+    const bf16x8 a = ld16<bf16x8>(xr + 8 * u);
+    const bf16x8 c = ld16<bf16x8>(xr + half + 8 * u);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      x1[p] = (float)a[p];
+      x2[p] = (float)c[p];
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) x1[p] = x2[p] = 0.f;
+  }
+  if (rp.rope && act) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) rope_pair(x1[p], x2[p], pos, rp.omega_rev[8 * u + p], false);
+  }
+  if (rp.qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) ss += x1[p] * x1[p] + x2[p] * x2[p];
+    ss += __shfl_xor(ss, 1, 8);
+    ss += __shfl_xor(ss, 2, 8);
+    ss += __shfl_xor(ss, 4, 8);
+    const float inv = 1.0f / sqrtf(ss / (float)D + rp.eps);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      x1[p] *= inv;
+      x2[p] *= inv;
+    }
+  }
+  if (act) {
+    bf16x8 a, c;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      a[p] = to_bf16(x1[p]);
+      c[p] = to_bf16(x2[p]);
+    }
+    const int64_t dst = (bg * Lmax + pos) * D;
+    *reinterpret_cast<bf16x8*>(kc + dst + 8 * u) = a;
+    *reinterpret_cast<bf16x8*>(kc + dst + half + 8 * u) = c;
+    const bf16* vr = vn + row * D;
+    *reinterpret_cast<bf16x8*>(vc + dst + 8 * u) = ld16<bf16x8>(vr + 8 * u);
+    *reinterpret_cast<bf16x8*>(vc + dst + half + 8 * u) = ld16<bf16x8>(vr + half + 8 * u);
+  }
+}
+
+hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
+                            const int32_t* cache_len, int B, int Hkv, int S, int Lmax, int D,
+                            int rope, float rope_base, int qk_norm, float eps, hipStream_t s) {
+  const int64_t rows = (int64_t)B * Hkv * S;
+  if (rows <= 0) return hipSuccess;
+  TraceScope t("append_kv", s);
+  hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s,
+                     (const bf16*)kn, (const bf16*)vn, (bf16*)kc, (bf16*)vc, cache_len, rows, S,
+                     Hkv, Lmax, D, make_row_prologue(rope, rope_base, qk_norm, eps, D));
+  return hipGetLastError();
+}
+
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

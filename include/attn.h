@@ -19,7 +19,8 @@
  * 181M model card ("Design choices worth naming") and on the flaxchat page ("Core
  * Features"), which also names the sliding window.  The KV-cache decode follows the
  * "Bonus: KV Caching" section of the GPT pretraining page: the new token's key/value are
- * already in the cache and its single query attends over the whole cached history.
+ * already in the cache and its single query attends over the whole cached history;
+ * attn_extend performs that section's whole step (append, then attend) for S new tokens.
  *
  * Conventions for every entry point below.
  *  - Pointers marked "device" are device memory owned by the caller; the library never
@@ -82,6 +83,21 @@ typedef struct {
   int32_t split_len;   /* keys per split-K chunk: 0 = library default, else a multiple of 64    */
 } attn_decode_cfg;
 
+/* Multi-token step against a KV cache (bfloat16 only): append, then attend. */
+typedef struct {
+  int32_t B;           /* sequences (>= 0)                                                      */
+  int32_t S;           /* new tokens per sequence (>= 0)                                        */
+  int32_t Hq, Hkv, D;  /* as in attn_cfg                                                        */
+  int32_t Lmax;        /* allocated cache rows per (b, kv head), >= 0                           */
+  int32_t window;      /* 0 = plain causal; W > 0: key j visible to position p iff p - W < j    */
+  float softcap;       /* as in attn_cfg                                                        */
+  float scale;         /* 0 = 1/sqrt(D)                                                         */
+  int32_t rope;        /* 1 = rotate the new queries and keys at their positions                */
+  float rope_base;
+  int32_t qk_norm;     /* 1 = RMSNorm the new queries and keys (cached keys are normalised)     */
+  float norm_eps;
+} attn_extend_cfg;
+
 /* Bytes of device workspace that attn_fwd / attn_bwd / attn_decode need for this
  * configuration (0 if none).  Host-only; returns 0 for an invalid configuration. */
 size_t attn_fwd_workspace_bytes(const attn_cfg* cfg);
@@ -92,6 +108,7 @@ size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg);
  * (before pointer and workspace checks).  for_backward = 1 applies the backward's rules. */
 int attn_check_cfg(const attn_cfg* cfg, int for_backward);
 int attn_check_decode_cfg(const attn_decode_cfg* cfg);
+int attn_check_extend_cfg(const attn_extend_cfg* cfg);
 
 /*
  * attn_fwd -- flash-style forward.
@@ -132,6 +149,30 @@ int attn_bwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, c
 int attn_decode(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* cache_len, void* o, void* ws,
                 size_t ws_bytes, void* stream);
+
+/*
+ * attn_extend -- S new tokens per sequence against its KV cache.  The "Bonus: KV Caching"
+ * section of the GPT pretraining page describes the step: compute the new tokens' keys and
+ * values, append them to the cache, and let the new queries attend over the whole cached
+ * history, query i seeing key j iff j <= offset + i with offset = the cached length.  With
+ * cache_len = 0 this is the causal forward of the S tokens (prefill); with S = 1 it is
+ * decode with the append done here.  bfloat16 only; no workspace.
+ *   q         [B, Hq, S, D] device, bf16 -- raw queries of the new tokens
+ *   k_new, v_new [B, Hkv, S, D] device, bf16 -- raw keys and values of the new tokens
+ *   k_cache, v_cache [B, Hkv, Lmax, D] device, bf16 -- rows < cache_len[b] hold the earlier
+ *             tokens' keys (rotated, and normalised when qk_norm = 1) and values.  Rows
+ *             cache_len[b] .. cache_len[b] + S - 1 are WRITTEN with the new tokens' keys
+ *             (rotated at their positions, normalised) and values; no other row is touched.
+ *   cache_len [B] device, int32 -- rows present before the call; not modified (the caller
+ *             adds S).  Values are clamped to [0, Lmax] in the kernels.
+ *   o         [B, Hq, S, D] device, bf16 (written) -- token i of sequence b sits at
+ *             position p = cache_len[b] + i and attends over rows j <= p (and j > p - W for
+ *             window = W > 0).  Tokens with p >= Lmax are neither stored nor attended:
+ *             their output rows are zero.
+ * q, k_new, v_new and o must not overlap the caches.
+ */
+int attn_extend(const attn_extend_cfg* cfg, const void* q, const void* k_new, const void* v_new,
+                void* k_cache, void* v_cache, const int32_t* cache_len, void* o, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(int status);

@@ -91,6 +91,26 @@ def test_decode_config_validation(L):
     assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 80, 2048, o))) == -2
 
 
+def test_extend_config_validation(L):
+    o = bd.AttnOptions(softcap=50.0, rope=True, qk_norm=True)
+    ok = bd.make_extend_cfg(4, 16, 8, 4, 96, 2048, o)
+    assert L.attn_check_extend_cfg(ctypes.byref(ok)) == bd.ATTN_OK
+    assert L.attn_check_extend_cfg(None) == bd.ATTN_EINVAL
+    bad = [bd.make_extend_cfg(4, -1, 8, 4, 96, 2048, o), bd.make_extend_cfg(4, 16, 8, 3, 96, 2048, o),
+           bd.make_extend_cfg(4, 16, 8, 4, 96, -1, o), bd.make_extend_cfg(-2, 16, 8, 4, 96, 64, o),
+           bd.make_extend_cfg(4, 16, 8, 4, 96, 64, bd.AttnOptions(window=-3)),
+           bd.make_extend_cfg(4, 16, 8, 4, 96, 64, bd.AttnOptions(qk_norm=True, norm_eps=0.0))]
+    for c in bad:
+        assert L.attn_check_extend_cfg(ctypes.byref(c)) == bd.ATTN_EINVAL
+    assert L.attn_check_extend_cfg(ctypes.byref(bd.make_extend_cfg(4, 16, 8, 4, 80, 64, o))) == \
+        bd.ATTN_EUNSUPPORTED
+    fake, null, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0), ctypes.c_void_p(0)
+    assert L.attn_extend(ctypes.byref(bad[1]), fake, fake, fake, fake, fake, fake, fake, s) == -1
+    assert L.attn_extend(ctypes.byref(ok), fake, fake, fake, fake, fake, null, fake, s) == -1
+    empty = bd.make_extend_cfg(4, 0, 8, 4, 96, 2048, o)
+    assert L.attn_extend(ctypes.byref(empty), null, null, null, null, null, null, null, s) == 0
+
+
 def test_entry_points_reject_before_launch(L):
     """Invalid configs, null pointers and short workspaces return an error status without
     any HIP call (this process has no GPU, so reaching one would fail differently)."""

@@ -10,9 +10,11 @@ import sys
 import numpy as np
 import pytest
 
-from causal_attention_02_amd import AttnOptions, attn_bwd, attn_decode, attn_fwd
-from causal_attention_02_amd.inputs import WORKLOADS, Workload, make_decode_inputs, make_train_inputs
-from oracle import attention_backward, attention_decode, attention_forward, rms_normalize, rope_rotate
+from causal_attention_02_amd import AttnOptions, attn_bwd, attn_decode, attn_extend, attn_fwd
+from causal_attention_02_amd.inputs import (WORKLOADS, Workload, make_decode_inputs,
+                                            make_train_inputs, round_to_bf16)
+from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
+                    rms_normalize, rope_rotate)
 from tests.util import (TOL_F32_MAXABS, TOL_GRAD, TOL_LSE_BF16, TOL_O, max_abs, rel_l2, to_dev,
                         to_host)
 
@@ -272,6 +274,84 @@ def test_decode_with_qk_norm():
 # --------------------------------------------------------------------------------------------
 # Error paths through the binding on a GPU (nothing is launched)
 # --------------------------------------------------------------------------------------------
+# --------------------------------------------------------------------------------------------
+# extend: S new tokens against a KV cache (append, then attend with the offset mask)
+# --------------------------------------------------------------------------------------------
+EXTEND_CASES = [
+    # B, S, Hq, Hkv, D, Lmax, cache lengths, options
+    (4, 37, 8, 4, 96, 300, [0, 100, 263, 290], dict(softcap=50.0, rope=True, qk_norm=True)),
+    (3, 130, 6, 3, 128, 600, [0, 250, 470], dict(window=200, rope=True, qk_norm=True)),
+    (6, 1, 4, 4, 64, 100, [0, 1, 50, 98, 99, 100], dict(softcap=20.0, rope=True)),
+    (2, 300, 4, 2, 32, 320, [0, 0], dict(rope=True, qk_norm=True, softcap=5.0)),
+    (2, 64, 2, 2, 128, 192, [17, 128], dict()),
+]
+
+
+@pytest.mark.parametrize("case", EXTEND_CASES, ids=[f"S{c[1]}_D{c[4]}" for c in EXTEND_CASES])
+def test_extend(case):
+    import torch
+    B, S, Hq, Hkv, D, Lmax, lens, flags = case
+    _say(f"case extend B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} Lmax={Lmax} lens={lens} {flags}")
+    rng = np.random.default_rng(1000 + S)
+    nrm = lambda *sh: round_to_bf16(rng.standard_normal(sh, dtype=np.float32))
+    q, kn, vn = nrm(B, Hq, S, D), nrm(B, Hkv, S, D), nrm(B, Hkv, S, D)
+    kc, vc = nrm(B, Hkv, Lmax, D), nrm(B, Hkv, Lmax, D)
+    if flags.get("qk_norm"):  # cached keys are stored normalised
+        kc = round_to_bf16(rms_normalize(kc)[0].astype(np.float32))
+    lens = np.array(lens, dtype=np.int32)
+    for b in range(B):  # rows the step must not read: poisoned
+        kc[b, :, lens[b]:] = np.nan
+        vc[b, :, lens[b]:] = np.nan
+    opts = AttnOptions(**flags)
+    tk, tv = to_dev(kc, torch.bfloat16), to_dev(vc, torch.bfloat16)
+    o = attn_extend(to_dev(q, torch.bfloat16), to_dev(kn, torch.bfloat16), to_dev(vn, torch.bfloat16),
+                    tk, tv, torch.from_numpy(lens).to("cuda"), opts)
+    torch.cuda.synchronize()
+    o, kg, vg = to_host(o), to_host(tk), to_host(tv)
+    ro, rk, rv = attention_extend(q, kn, vn, kc, vc, lens, **flags)
+    assert np.isfinite(o).all()
+    e = rel_l2(o, ro)
+    _say(f"extend relL2(o)={e:.2e}")
+    assert e <= TOL_O
+    for b in range(B):
+        n = max(0, min(S, Lmax - int(lens[b])))
+        np.testing.assert_array_equal(o[b, :, n:], 0.0)  # tokens past Lmax
+        new = slice(int(lens[b]), int(lens[b]) + n)
+        if n:
+            assert rel_l2(kg[b, :, new], rk[b, :, new]) <= 1e-2  # keys rotated/normalised, bf16
+            np.testing.assert_array_equal(vg[b, :, new], rv[b, :, new])
+        # Every other row is bitwise untouched (NaN rows stay NaN).
+        np.testing.assert_array_equal(kg[b, :, :int(lens[b])], kc[b, :, :int(lens[b])])
+        np.testing.assert_array_equal(np.isnan(kg[b, :, new.stop:]), True)
+        np.testing.assert_array_equal(np.isnan(vg[b, :, new.stop:]), True)
+
+
+def test_extend_then_decode_matches_forward():
+    """Prefill T - 1 tokens with extend, then decode the last token: the last row of the
+    forward over the whole sequence (the GPT pretraining page's KV-cache consistency)."""
+    import torch
+    w = Workload("ext", B=3, T=200, Hq=8, Hkv=4, D=96, softcap=50.0, rope=True, qk_norm=True,
+                 backward=False, seed=77)
+    q, k, v, _ = make_train_inputs(w)
+    opts = opts_of(w)
+    Lmax = 256
+    tk = torch.zeros((w.B, w.Hkv, Lmax, w.D), dtype=torch.bfloat16, device="cuda")
+    tv = torch.zeros_like(tk)
+    lens = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    qd, kd, vd = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    o1 = attn_extend(qd[:, :, :-1].contiguous(), kd[:, :, :-1].contiguous(),
+                     vd[:, :, :-1].contiguous(), tk, tv, lens, opts)
+    lens += w.T - 1
+    o2 = attn_extend(qd[:, :, -1:].contiguous(), kd[:, :, -1:].contiguous(),
+                     vd[:, :, -1:].contiguous(), tk, tv, lens, opts)
+    torch.cuda.synchronize()
+    got = np.concatenate([to_host(o1), to_host(o2)], axis=2)
+    ref, _ = attention_forward(q, k, v, **oracle_kw(w))
+    e = rel_l2(got, ref)
+    _say(f"extend chain relL2={e:.2e}")
+    assert e <= TOL_O
+
+
 def test_errors_on_gpu():
     import torch
     from causal_attention_02_amd import AttnError
