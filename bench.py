@@ -92,6 +92,7 @@ def main():
 
     from causal_attention_02_amd import binding as bd
     from causal_attention_02_amd.inputs import (WORKLOADS, decode_bytes, make_decode_inputs,
+                                                extend_flops, make_extend_inputs,
                                                 make_train_inputs, train_flops, visible_pairs)
 
     if not torch.cuda.is_available():
@@ -274,6 +275,26 @@ def main():
         extra["gpt_pretrain_decode"] = dict(us_per_call=us_s,
                                             GBps=decode_bytes(ws, lens_s) / (us_s * 1e-6) / 1e9)
         log(f"[bench] gpt_pretrain_decode: {us_s:.1f} us/call")
+        # Multi-token step (append + attend) on decode-sized caches.
+        we = WORKLOADS["gqa181m_extend"]
+        qe, kne, vne, kce, vce, lens_e = make_extend_inputs(we)
+        tqe, tkne, tvne, tkce, tvce = (to_dev(x) for x in (qe, kne, vne, kce, vce))
+        tle = torch.from_numpy(lens_e).to(dev)
+        oe = torch.empty_like(tqe)
+        opts_e = opts_of(we)
+        for _ in range(5):
+            bd.attn_extend(tqe, tkne, tvne, tkce, tvce, tle, opts_e, out=oe)
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for _ in range(n):
+            bd.attn_extend(tqe, tkne, tvne, tkce, tvce, tle, opts_e, out=oe)
+        evs[1].record(stream)
+        torch.cuda.synchronize()
+        us_e = evs[0].elapsed_time(evs[1]) / n * 1e3
+        tf_e = extend_flops(we, lens_e) / (us_e * 1e-6) / 1e12
+        extra["gqa181m_extend"] = dict(us_per_call=us_e, tflops=tf_e,
+                                       pct_peak=100 * tf_e / PEAK_BF16_TFLOPS)
+        log(f"[bench] gqa181m_extend: {us_e:.1f} us/call  {tf_e:.1f} TFLOP/s")
         if "value" not in result:
             result.update(value=gbs, ms_per_step=ms_d)
 

@@ -51,6 +51,8 @@ class Workload:
     backward: bool = True
     decode: bool = False         # single-token KV-cache decode instead of fwd/bwd
     len_lo: int = 0              # decode: cache lengths ~ U{len_lo .. T}
+    new_tokens: int = 0          # extend: tokens appended per sequence (cache lengths ~
+                                 # U{len_lo .. T - new_tokens}, T = allocated rows)
     seed: int = SEED_BASE
     note: str = field(default="", compare=False)
 
@@ -80,6 +82,11 @@ WORKLOADS = {
     "gqa181m_decode": Workload("gqa181m_decode", B=64, T=2048, Hq=8, Hkv=4, D=96, softcap=50.0,
                                rope=True, backward=False, decode=True, len_lo=256,
                                seed=SEED_BASE + 4),
+    # A multi-token step on the decode caches: 128 new tokens per sequence (chunked prefill or
+    # speculative verification) against cache lengths U{256..1920}.
+    "gqa181m_extend": Workload("gqa181m_extend", B=64, T=2048, Hq=8, Hkv=4, D=96, softcap=50.0,
+                               rope=True, backward=False, len_lo=256, new_tokens=128,
+                               seed=SEED_BASE + 8),
     # GPT pretraining page: 768 dims over 12 heads -> d = 64, context 256, batch 128; plain
     # causal multi-head attention (learned position embeddings, no RoPE / QK-norm / cap).
     "gpt_pretrain_train": Workload("gpt_pretrain_train", B=128, T=256, Hq=12, Hkv=12, D=64,
@@ -124,6 +131,27 @@ def make_decode_inputs(w: Workload, seed: int | None = None):
     kc = _normal(rng, (w.B, w.Hkv, w.T, w.D), True)
     vc = _normal(rng, (w.B, w.Hkv, w.T, w.D), True)
     return q, kc, vc, cache_len
+
+
+def make_extend_inputs(w: Workload, seed: int | None = None):
+    """q [B,Hq,S,D], k_new/v_new [B,Hkv,S,D], caches [B,Hkv,Lmax,D] (float32, bf16-exact) and
+    cache_len int32 [B] ~ U{len_lo .. Lmax - S}; S = w.new_tokens, Lmax = w.T."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    S = w.new_tokens
+    cache_len = rng.integers(w.len_lo, w.T - S, size=w.B, endpoint=True).astype(np.int32)
+    q = _normal(rng, (w.B, w.Hq, S, w.D), True)
+    kn = _normal(rng, (w.B, w.Hkv, S, w.D), True)
+    vn = _normal(rng, (w.B, w.Hkv, S, w.D), True)
+    kc = _normal(rng, (w.B, w.Hkv, w.T, w.D), True)
+    vc = _normal(rng, (w.B, w.Hkv, w.T, w.D), True)
+    return q, kn, vn, kc, vc, cache_len
+
+
+def extend_flops(w: Workload, cache_len) -> float:
+    """4 d flops per visible (new query, key) pair: query i of sequence b sees L_b + i + 1 keys."""
+    S = w.new_tokens
+    pairs = sum(S * int(L) + S * (S + 1) // 2 for L in cache_len)
+    return 4.0 * w.D * w.Hq * pairs
 
 
 def visible_pairs(T: int, window: int = 0) -> int:

@@ -12,7 +12,7 @@ import pytest
 
 from causal_attention_02_amd import AttnOptions, attn_bwd, attn_decode, attn_extend, attn_fwd
 from causal_attention_02_amd.inputs import (WORKLOADS, Workload, make_decode_inputs,
-                                            make_train_inputs, round_to_bf16)
+                                            make_extend_inputs, make_train_inputs, round_to_bf16)
 from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
                     rms_normalize, rope_rotate)
 from tests.util import (TOL_F32_MAXABS, TOL_GRAD, TOL_LSE_BF16, TOL_O, max_abs, rel_l2, to_dev,
@@ -324,6 +324,30 @@ def test_extend(case):
         np.testing.assert_array_equal(kg[b, :, :int(lens[b])], kc[b, :, :int(lens[b])])
         np.testing.assert_array_equal(np.isnan(kg[b, :, new.stop:]), True)
         np.testing.assert_array_equal(np.isnan(vg[b, :, new.stop:]), True)
+
+
+def test_extend_full_size_sampled():
+    """The bench's multi-token workload (64 sequences x 128 new tokens on 2048-row caches):
+    sampled sequences against the oracle."""
+    import torch
+    w = WORKLOADS["gqa181m_extend"]
+    _say(f"case {w.name}: B={w.B} S={w.new_tokens} Lmax={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
+    q, kn, vn, kc, vc, lens = make_extend_inputs(w)
+    tk, tv = to_dev(kc, torch.bfloat16), to_dev(vc, torch.bfloat16)
+    o = attn_extend(to_dev(q, torch.bfloat16), to_dev(kn, torch.bfloat16),
+                    to_dev(vn, torch.bfloat16), tk, tv, torch.from_numpy(lens).to("cuda"),
+                    opts_of(w))
+    torch.cuda.synchronize()
+    o, kg = to_host(o), to_host(tk)
+    kw = {a: b for a, b in oracle_kw(w).items()}
+    for b in (0, w.B // 2, w.B - 1):
+        sl = slice(b, b + 1)
+        ro, rk, _ = attention_extend(q[sl], kn[sl], vn[sl], kc[sl], vc[sl], lens[sl], **kw)
+        e = rel_l2(o[sl], ro)
+        L = int(lens[b])
+        ek = rel_l2(kg[sl][:, :, L:L + w.new_tokens], rk[:, :, L:L + w.new_tokens])
+        _say(f"{w.name}[b={b}, L={L}]: relL2(o)={e:.2e} relL2(k rows)={ek:.2e}")
+        assert e <= TOL_O and ek <= 1e-2
 
 
 def test_extend_then_decode_matches_forward():
