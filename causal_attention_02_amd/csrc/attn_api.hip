@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -130,12 +131,14 @@ float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf(
 
 // Default chunking: enough (b, kv head, head subset, chunk) workgroups to cover about 256
 // compute units even if every cache were full; one chunk per sequence when the batch alone
-// does that (then no merge pass is needed).
+// does that (then no merge pass is needed).  At most 16 chunks per sequence: the merge reads
+// the chunks of a row one after another, and beyond that it costs more than it saves.
 int decode_split_len(const attn_decode_cfg* c) {
   if (c->split_len > 0) return c->split_len;
   const long units = (long)c->B * c->Hkv * (c->Hq / c->Hkv / decode_heads_per_block(c->Hq / c->Hkv, c->D));
   const long want = units >= 256 ? 1 : (256 + units - 1) / units;
   long len = c->Lmax > 0 ? (c->Lmax + want - 1) / want : 64;
+  len = std::max(len, (c->Lmax + 15L) / 16);
   len = (len + 63) / 64 * 64;
   return (int)(len > 0 ? len : 64);
 }

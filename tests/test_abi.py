@@ -75,9 +75,12 @@ def test_workspace_sizes(L):
     # Default chunking: 64 x 4 (b, kv head) workgroups already cover the GPU -> one chunk.
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(softcap=50.0, rope=True))
     assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 1 * 98 * 4
-    # One sequence: 4 (b, kv head) units -> 64 chunks of 64 rows over a 4096-row cache.
+    # One sequence: 4 (b, kv head) units would want 64 chunks; capped at 16 (256 rows each).
     d = bd.make_decode_cfg(1, 8, 4, 96, 4096, bd.AttnOptions())
-    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 1 * 8 * 64 * 98 * 4
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 1 * 8 * 16 * 98 * 4
+    # A 256-row cache of one sequence keeps 4 chunks of 64 rows.
+    d = bd.make_decode_cfg(1, 12, 12, 64, 256, bd.AttnOptions())
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == (1 * 12 * 4 * 66 * 4 + 255) // 256 * 256
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(), split_len=128)
     assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 16 * 98 * 4
 
