@@ -7,5 +7,6 @@ from .attn_ref import (  # noqa: F401
     rms_normalize,
     rope_rotate,
     rope_unrotate,
+    segment_starts,
     visible_mask,
 )

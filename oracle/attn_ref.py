@@ -40,6 +40,12 @@ project's design notes):
 * Decode: the cache already holds the new token's (rotated) key/value, so the query
   sits at position L_b - 1 and sees all L_b cached keys; a sequence with L_b = 0
   yields an all-zero output row.
+* Packed rows (segment_ids): a segment is a maximal run of equal ids in a row; a token
+  attends only to keys of its own run, and its RoPE position is its offset from the start
+  of the run (nanoGPT-JAX 181M model card, SFT notes: packed rows with segment ids, RoPE
+  from packed segment positions).  Scores see RoPE only through position differences and
+  RMSNorm commutes with the rotation, so restarting positions at each run changes no
+  output or gradient here; it matters for keys that are stored rotated (a KV cache).
 * Extend: cache_len counts the rows present before the step; new token i sits at
   position L_b + i, its key is rotated at that position (and normalised) before it
   is stored, and rows that would land at or past Lmax are not stored (their queries
@@ -57,6 +63,7 @@ __all__ = [
     "rope_unrotate",
     "rms_normalize",
     "visible_mask",
+    "segment_starts",
     "attention_forward",
     "attention_backward",
     "attention_decode",
@@ -147,6 +154,25 @@ def visible_mask(T: int, window: int = 0) -> np.ndarray:
     return m
 
 
+def segment_starts(ids) -> np.ndarray:
+    """Index of the first token of each token's segment (a maximal run of equal ids)."""
+    ids = np.asarray(ids)
+    start = np.zeros(len(ids), dtype=np.int64)
+    for i in range(1, len(ids)):
+        start[i] = i if ids[i] != ids[i - 1] else start[i - 1]
+    return start
+
+
+def _row_layout(T, window, segment_ids, b):
+    """Positions and visibility of row b: absolute positions and the causal (window) mask,
+    or, for packed rows, offsets within each segment and the mask restricted to the segment."""
+    allowed = visible_mask(T, window)
+    if segment_ids is None:
+        return np.arange(T), allowed
+    start = segment_starts(segment_ids[b])
+    return np.arange(T) - start, allowed & (np.arange(T)[None, :] >= start[:, None])
+
+
 def _scores(qh, kh, scale, softcap):
     """Scaled scores and their soft-capped version for one (b, h): both [Tq, Tk]."""
     s_pre = scale * (qh @ kh.T)
@@ -177,11 +203,12 @@ def _check_shapes(q, k, v):
 
 
 def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
-                      rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+                      rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None):
     """Causal attention forward for q [B,Hq,T,d], k/v [B,Hkv,T,d]; returns (O [B,Hq,T,d], LSE [B,Hq,T]).
 
     Per (b, h):  q^ = prologue(q), k^ = prologue(k);  S = scale * q^ k^T;  S <- c tanh(S / c)
     if capped;  masked entries -> -inf;  P = row softmax(S);  O = P V;  LSE = ln sum_j exp(S_ij).
+    segment_ids [B, T] (optional): packed rows, see the module notes.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -190,11 +217,10 @@ def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
     if scale is None or scale == 0:
         scale = 1.0 / np.sqrt(d)
     group = Hq // Hkv
-    pos = np.arange(T)
-    allowed = visible_mask(T, window)
     O = np.empty((B, Hq, T, d))
     LSE = np.empty((B, Hq, T))
     for b in range(B):
+        pos, allowed = _row_layout(T, window, segment_ids, b)
         khat = [_prologue(k[b, g], pos, rope, rope_base, qk_norm, norm_eps)[0] for g in range(Hkv)]
         for h in range(Hq):
             g = h // group
@@ -207,7 +233,7 @@ def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
 
 
 def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=False,
-                       rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+                       rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None):
     """Analytic gradients (dQ, dK, dV) of <O, dO> with respect to the RAW q, k, v.
 
     Per (b, h) with g = kv head of h:
@@ -226,12 +252,11 @@ def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=F
     if scale is None or scale == 0:
         scale = 1.0 / np.sqrt(d)
     group = Hq // Hkv
-    pos = np.arange(T)
-    allowed = visible_mask(T, window)
     dQ = np.empty_like(q)
     dK = np.zeros_like(k)
     dV = np.zeros_like(v)
     for b in range(B):
+        pos, allowed = _row_layout(T, window, segment_ids, b)
         kpro = [_prologue(k[b, g], pos, rope, rope_base, qk_norm, norm_eps) for g in range(Hkv)]
         dkhat = [np.zeros((T, d)) for _ in range(Hkv)]
         for h in range(Hq):

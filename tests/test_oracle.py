@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
-                    rms_normalize, rope_rotate, rope_unrotate, visible_mask)
+                    rms_normalize, rope_rotate, rope_unrotate, segment_starts, visible_mask)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -359,6 +359,94 @@ def test_decode_zero_length_and_clamp():
     np.testing.assert_array_equal(o[1], 0.0)
     o_full = attention_decode(q[2:], kc[2:], vc[2:], np.array([6]))
     np.testing.assert_allclose(o[2], o_full[0], atol=0)
+
+
+# ------------------------------------------------------------------------------------
+# Packed rows: segment ids restrict attention to a token's own run; RoPE restarts per run.
+# ------------------------------------------------------------------------------------
+def test_segment_starts_examples():
+    np.testing.assert_array_equal(segment_starts([7, 7, 3, 3, 3, 7]), [0, 0, 2, 2, 2, 5])
+    np.testing.assert_array_equal(segment_starts([1]), [0])
+    np.testing.assert_array_equal(segment_starts([0, 1, 2]), [0, 1, 2])
+    np.testing.assert_array_equal(segment_starts([4, 4, 4]), [0, 0, 0])
+
+
+def _packed_case(rng, B, Hq, Hkv, lengths, d):
+    T = sum(lengths)
+    q, k, v, dO = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hq, T, d)
+    ids = np.concatenate([np.full(n, i % 3) for i, n in enumerate(lengths)])  # runs of 0,1,2,0,..
+    return q, k, v, dO, np.tile(ids, (B, 1))
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_packed_rows_equal_separate_sequences(flags):
+    """A packed row is block-diagonal: each run gives what the same tokens give alone."""
+    rng = np.random.default_rng(31)
+    lengths = [5, 1, 7, 3]
+    q, k, v, dO, ids = _packed_case(rng, 2, 4, 2, lengths, 8)
+    O, L = attention_forward(q, k, v, segment_ids=ids, **flags)
+    dQ, dK, dV = attention_backward(q, k, v, dO, segment_ids=ids, **flags)
+    a = 0
+    for n in lengths:
+        sl = slice(a, a + n)
+        Os, Ls = attention_forward(q[:, :, sl], k[:, :, sl], v[:, :, sl], **flags)
+        gs = attention_backward(q[:, :, sl], k[:, :, sl], v[:, :, sl], dO[:, :, sl], **flags)
+        np.testing.assert_allclose(O[:, :, sl], Os, atol=1e-13)
+        np.testing.assert_allclose(L[:, :, sl], Ls, atol=1e-13)
+        for g, r in zip((dQ, dK, dV), gs):
+            np.testing.assert_allclose(g[:, :, sl], r, atol=1e-12)
+        a += n
+
+
+def test_packed_rows_match_brute_force():
+    rng = np.random.default_rng(32)
+    q, k, v, _, ids = _packed_case(rng, 1, 2, 1, [3, 4, 2], 6)
+    flags = dict(window=3, softcap=2.0, rope=True, qk_norm=True)
+    O, _ = attention_forward(q, k, v, segment_ids=ids, **flags)
+    T, d = q.shape[2], q.shape[3]
+    start = [0, 0, 0, 3, 3, 3, 3, 7, 7]
+    for h, i in itertools.product(range(2), range(T)):
+        qi = _bf_prologue(q[0, h, i], i - start[i], True, 10000.0, True, 1e-6)
+        keys = [j for j in range(start[i], i + 1) if i - j < 3]
+        sc = []
+        for j in keys:
+            kj = _bf_prologue(k[0, 0, j], j - start[j], True, 10000.0, True, 1e-6)
+            s_ = sum(a * c for a, c in zip(qi, kj)) / math.sqrt(d)
+            sc.append(2.0 * math.tanh(s_ / 2.0))
+        w = [math.exp(x - max(sc)) for x in sc]
+        ref = sum(wj / sum(w) * v[0, 0, j] for wj, j in zip(w, keys))
+        np.testing.assert_allclose(O[0, h, i], ref, atol=1e-12)
+
+
+def test_packed_gradients_match_finite_differences():
+    rng = np.random.default_rng(33)
+    q, k, v, dO, ids = _packed_case(rng, 1, 2, 1, [2, 3, 2], 4)
+    flags = dict(window=0, softcap=1.5, rope=True, qk_norm=True)
+    grads = attention_backward(q, k, v, dO, segment_ids=ids, **flags)
+    f = lambda qq, kk, vv: float(np.sum(attention_forward(qq, kk, vv, segment_ids=ids, **flags)[0] * dO))
+    eps = 1e-6
+    for which, x in enumerate((q, k, v)):
+        for idx in [(0, 0, 1, 2), (0, 0, 4, 0), (0, 0, 6, 3)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num = (f(*args_p) - f(*args_m)) / (2 * eps)
+            np.testing.assert_allclose(grads[which][idx], num, rtol=1e-6, atol=1e-8)
+
+
+def test_single_run_is_plain_attention():
+    rng = np.random.default_rng(34)
+    q, k, v, dO = rnd(rng, 2, 2, 9, 8), rnd(rng, 2, 1, 9, 8), rnd(rng, 2, 1, 9, 8), rnd(rng, 2, 2, 9, 8)
+    ids = np.full((2, 9), 5)
+    flags = dict(softcap=3.0, rope=True, qk_norm=True)
+    np.testing.assert_allclose(attention_forward(q, k, v, segment_ids=ids, **flags)[0],
+                               attention_forward(q, k, v, **flags)[0], atol=0)
+    for a, b in zip(attention_backward(q, k, v, dO, segment_ids=ids, **flags),
+                    attention_backward(q, k, v, dO, **flags)):
+        np.testing.assert_allclose(a, b, atol=0)
 
 
 # ------------------------------------------------------------------------------------
