@@ -19,8 +19,10 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = [
     "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes",
+    "attn_fwd_packed_workspace_bytes", "attn_bwd_packed_workspace_bytes",
     "attn_check_cfg", "attn_check_decode_cfg", "attn_check_extend_cfg", "attn_fwd", "attn_bwd",
-    "attn_decode", "attn_extend", "attn_status_str", "attn_trace_enable", "attn_trace_read",
+    "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
+    "attn_trace_enable", "attn_trace_read",
 ]
 
 
@@ -77,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_workspace_bytes.restype = sz
         L.attn_bwd_workspace_bytes.argtypes = [cfgp]
         L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_fwd_packed_workspace_bytes.argtypes = [cfgp]
+        L.attn_fwd_packed_workspace_bytes.restype = sz
+        L.attn_bwd_packed_workspace_bytes.argtypes = [cfgp]
+        L.attn_bwd_packed_workspace_bytes.restype = sz
         L.attn_decode_workspace_bytes.argtypes = [dcfgp]
         L.attn_decode_workspace_bytes.restype = sz
         L.attn_check_cfg.argtypes = [cfgp, ctypes.c_int]
@@ -89,6 +95,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = ctypes.c_int
         L.attn_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_bwd.restype = ctypes.c_int
+        L.attn_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_fwd_packed.restype = ctypes.c_int
+        L.attn_bwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_bwd_packed.restype = ctypes.c_int
         L.attn_decode.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_decode.restype = ctypes.c_int
         L.attn_extend.argtypes = [ecfgp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -198,8 +208,11 @@ def bwd_workspace_bytes(B, T, Hq, Hkv, D, opts: AttnOptions) -> int:
 
 
 def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, workspace=None,
-             stream=None):
-    """Forward: q [B,Hq,T,D], k/v [B,Hkv,T,D] (bf16 or fp32) -> (o, lse fp32 [B,Hq,T])."""
+             stream=None, segment_ids=None):
+    """Forward: q [B,Hq,T,D], k/v [B,Hkv,T,D] (bf16 or fp32) -> (o, lse fp32 [B,Hq,T]).
+
+    segment_ids (int32 [B,T], optional): packed rows; attention stays inside each run of equal
+    ids (bf16 only)."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, T, D = q.shape
@@ -215,6 +228,16 @@ def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, wo
     cfg = make_cfg(B, T, Hq, Hkv, D, opts, dt)
     st = lib().attn_check_cfg(ctypes.byref(cfg), 0)
     _check(st, "attn_fwd")
+    if segment_ids is not None:
+        _need(segment_ids, (B, T), torch.int32, "segment_ids")
+        ws = _workspace(int(lib().attn_fwd_packed_workspace_bytes(ctypes.byref(cfg))), q.device,
+                        workspace)
+        st = lib().attn_fwd_packed(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(segment_ids),
+                                   _ptr(o), _ptr(lse_t), _ptr(ws),
+                                   ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+                                   _stream(stream))
+        _check(st, "attn_fwd_packed")
+        return o, lse_t
     ws = _workspace(int(lib().attn_fwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
     st = lib().attn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(ws),
                         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
@@ -224,8 +247,9 @@ def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, wo
 
 
 def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
-    """Backward (bf16): returns (dq, dk, dv) with respect to the raw q, k, v."""
+             workspace=None, stream=None, segment_ids=None):
+    """Backward (bf16): returns (dq, dk, dv) with respect to the raw q, k, v (packed rows with
+    segment_ids as in attn_fwd)."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, T, D = q.shape
@@ -243,6 +267,17 @@ def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, d
     _need(dv, v.shape, bf, "dv")
     cfg = make_cfg(B, T, Hq, Hkv, D, opts, ATTN_BF16)
     _check(lib().attn_check_cfg(ctypes.byref(cfg), 1), "attn_bwd")
+    if segment_ids is not None:
+        _need(segment_ids, (B, T), torch.int32, "segment_ids")
+        ws = _workspace(int(lib().attn_bwd_packed_workspace_bytes(ctypes.byref(cfg))), q.device,
+                        workspace)
+        st = lib().attn_bwd_packed(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                                   _ptr(lse), _ptr(segment_ids), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(ws),
+                                   ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+                                   _stream(stream))
+        _check(st, "attn_bwd_packed")
+        return dq, dk, dv
     ws = _workspace(int(lib().attn_bwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
     st = lib().attn_bwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),

@@ -170,6 +170,9 @@ size_t bwd_ws(const attn_cfg* c) {
   return s;
 }
 
+// Packed rows: run starts and ends, [B, T] int32 each.
+size_t seg_ws(const attn_cfg* c) { return 2 * align_up((size_t)c->B * c->T * 4); }
+
 size_t dec_ws(const attn_decode_cfg* c) {
   return align_up((size_t)c->B * c->Hq * decode_nsplit(c) * (c->D + 2) * 4);
 }
@@ -201,17 +204,27 @@ size_t attn_fwd_workspace_bytes(const attn_cfg* cfg) {
 size_t attn_bwd_workspace_bytes(const attn_cfg* cfg) {
   return check_cfg(cfg, 1) == ATTN_OK ? bwd_ws(cfg) : 0;
 }
+size_t attn_fwd_packed_workspace_bytes(const attn_cfg* cfg) {
+  return check_cfg(cfg, 0) == ATTN_OK ? fwd_ws(cfg) + seg_ws(cfg) : 0;
+}
+size_t attn_bwd_packed_workspace_bytes(const attn_cfg* cfg) {
+  return check_cfg(cfg, 1) == ATTN_OK ? bwd_ws(cfg) + seg_ws(cfg) : 0;
+}
 size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg) {
   return check_dcfg(cfg) == ATTN_OK ? dec_ws(cfg) : 0;
 }
 
-int attn_fwd(const attn_cfg* c, const void* q, const void* k, const void* v, void* o, float* lse,
-             void* ws, size_t ws_bytes, void* stream) {
+// Forward and backward bodies; `ids` (segment ids [B, T], or null) selects packed rows, whose
+// run starts (and ends) go to a region after the plain workspace.
+static int fwd_impl(const attn_cfg* c, const void* q, const void* k, const void* v,
+                    const int32_t* ids, void* o, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
   int st = check_cfg(c, 0);
   if (st != ATTN_OK) return st;
+  if (ids && c->dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (c->B == 0 || c->T == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
-  const size_t need = fwd_ws(c);
+  const size_t need = fwd_ws(c) + (ids ? seg_ws(c) : 0);
   if (need > 0 && (!ws || ws_bytes < need)) return ATTN_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const bool pro = c->rope || c->qk_norm;
@@ -220,14 +233,20 @@ int attn_fwd(const attn_cfg* c, const void* q, const void* k, const void* v, voi
               eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
               c->norm_eps};
   hipError_t e = hipSuccess;
-  if (c->dtype == ATTN_BF16) {
+  if (ids) {
+    int32_t* sst = (int32_t*)((char*)ws + fwd_ws(c));
+    int32_t* sen = (int32_t*)((char*)sst + align_up((size_t)c->B * c->T * 4));
+    e = launch_segment_bounds(ids, sst, sen, c->B, c->T, s);
+    p.seg_start = sst;
+  }
+  if (e == hipSuccess && c->dtype == ATTN_BF16) {
     if (pro) {
       e = launch_prologue(k, ws, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
                           c->norm_eps, s);
       p.k = ws;
     }
     if (e == hipSuccess) e = launch_fwd_bf16(p, s);
-  } else {
+  } else if (e == hipSuccess) {
     if (pro) {
       char* w = (char*)ws;
       void* kw = w + align_up((size_t)qrows * c->D * 4);
@@ -244,14 +263,14 @@ int attn_fwd(const attn_cfg* c, const void* q, const void* k, const void* v, voi
   return launch_status(e);
 }
 
-int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, const void* o,
-             const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
-             size_t ws_bytes, void* stream) {
+static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void* v,
+                    const void* o, const void* dO, const float* lse, const int32_t* ids,
+                    void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
   int st = check_cfg(c, 1);
   if (st != ATTN_OK) return st;
   if (c->B == 0 || c->T == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_EINVAL;
-  const size_t need = bwd_ws(c);
+  const size_t need = bwd_ws(c) + (ids ? seg_ws(c) : 0);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int64_t qrows = (int64_t)c->B * c->Hq * c->T, krows = (int64_t)c->B * c->Hkv * c->T;
@@ -275,9 +294,41 @@ int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, con
   BwdParams p{q, k, kh, qh, v, o, dO, lse, Dvec, L2, dq, dk, dv, c->B, c->T, c->Hq, c->Hkv, c->D,
               c->window, eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base,
               c->qk_norm, c->norm_eps};
+  if (ids && e == hipSuccess) {
+    int32_t* sst = (int32_t*)((char*)ws + bwd_ws(c));
+    int32_t* sen = (int32_t*)((char*)sst + align_up((size_t)c->B * c->T * 4));
+    e = launch_segment_bounds(ids, sst, sen, c->B, c->T, s);
+    p.seg_start = sst;
+    p.seg_end = sen;
+  }
   if (e == hipSuccess) e = launch_bwd_dq(p, s);
   if (e == hipSuccess) e = launch_bwd_dkdv(p, s);
   return launch_status(e);
+}
+
+int attn_fwd(const attn_cfg* c, const void* q, const void* k, const void* v, void* o, float* lse,
+             void* ws, size_t ws_bytes, void* stream) {
+  return fwd_impl(c, q, k, v, nullptr, o, lse, ws, ws_bytes, stream);
+}
+
+int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, const void* o,
+             const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
+             size_t ws_bytes, void* stream) {
+  return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+int attn_fwd_packed(const attn_cfg* c, const void* q, const void* k, const void* v,
+                    const int32_t* segment_ids, void* o, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!segment_ids && c && c->B > 0 && c->T > 0) return ATTN_EINVAL;
+  return fwd_impl(c, q, k, v, segment_ids, o, lse, ws, ws_bytes, stream);
+}
+
+int attn_bwd_packed(const attn_cfg* c, const void* q, const void* k, const void* v,
+                    const void* o, const void* dO, const float* lse, const int32_t* segment_ids,
+                    void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  if (!segment_ids && c && c->B > 0 && c->T > 0) return ATTN_EINVAL;
+  return bwd_impl(c, q, k, v, o, dO, lse, segment_ids, dq, dk, dv, ws, ws_bytes, stream);
 }
 
 int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, const void* v_cache,

@@ -44,6 +44,8 @@ struct BwdArgs {
   const float* lse;
   float* Dvec;
   float* L2;  // LSE * log2(e) per query row (written by dq for dkdv)
+  const int32_t* seg_start;  // packed rows: first / last index of each token's run, [B, T]
+  const int32_t* seg_end;    // (null: one run per row)
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -123,6 +125,9 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   const int qrow = min(qi, T - 1);
   const int window = a.window;
   const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
+  // Packed rows: this lane's query sees keys back to the start of its run only.
+  const int32_t* sst = a.seg_start ? a.seg_start + (int64_t)b * T : nullptr;
+  const unsigned lim = sst ? min(wlim, (unsigned)(qrow - sst[qrow] + 1)) : wlim;
   const bf16* kbase = a.kh + (int64_t)(b * a.Hkv + g) * T * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * T * D;
   const int64_t rowoff = ((int64_t)bh * T + qrow) * D;
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   if (gl == 0 && qi < T) a.L2[(int64_t)bh * T + qi] = lse2;
 
   const int k_end = min(T, q0 + kBMq);
-  const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
+  const int k_begin = max(window > 0 ? max(0, q0 - window + 1) : 0, sst ? sst[q0] : 0);
   const int kt0 = k_begin / kBNk, kt1 = (k_end - 1) / kBNk;
 
   // Rows past T read clamped, finite data that the causal mask removes.
@@ -183,6 +188,8 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
 
   const bool wave_active = qw0 < T;
   const int qw_last = min(qw0 + 31, T - 1);
+  // Earliest and latest run start among the wave's queries (packed rows).
+  const int s_lo = sst ? sst[min(qw0, T - 1)] : 0, s_hi = sst ? sst[qw_last] : 0;
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
@@ -191,10 +198,11 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   // The phase fences keep one phase's registers live at a time (two waves share a SIMD).
   auto run = [&](int kt, const bf16* sk, const bf16* sv) {
     const int k0 = kt * kBNk;
-    const bool skip = !wave_active || k0 > qw_last ||
+    const bool skip = !wave_active || k0 > qw_last || k0 + kBNk - 1 < s_lo ||
                       (window > 0 && k0 + kBNk - 1 < qw0 - window + 1);
     if (skip) return;
-    const bool need_mask = (k0 + kBNk - 1 > qw0) || (window > 0 && k0 < qw_last - window + 1);
+    const bool need_mask = (k0 + kBNk - 1 > qw0) || k0 < s_hi ||
+                           (window > 0 && k0 < qw_last - window + 1);
     // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
     const int qd = qi - k0 - 4 * gl;
     f32x16 sacc[2], pacc[2];
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
             float gf;
             float y = score_grad<MODE>(sacc[kb][r], a.sc, lse2, &gf);
             if constexpr (decltype(masked)::value)
-              y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
+              y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
             float p = exp2_fast(y);
             if constexpr (MODE != kScoreScale) p *= gf;
             sacc[kb][r] = p * pacc[kb][r];
@@ -305,9 +313,12 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
   const int kj = kw0 + lr;
   const int krow = min(kj, T - 1);
   const int window = a.window;
-  // Query i sees this lane's key j iff 0 <= i - j < lim: the causal / window rule plus
-  // i < T (query rows past T are clamped copies of row T - 1 and must get P = 0).
-  const unsigned lim = (unsigned)min(window > 0 ? window : 0x7fffffff, max(T - kj, 0));
+  // Query i sees this lane's key j iff 0 <= i - j < lim: the causal / window rule, i < T
+  // (query rows past T are clamped copies of row T - 1 and must get P = 0) and, for packed
+  // rows, i <= the last index of the key's run.
+  const int32_t* sen = a.seg_end ? a.seg_end + (int64_t)b * T : nullptr;
+  const unsigned lim = (unsigned)min(min(window > 0 ? window : 0x7fffffff, max(T - kj, 0)),
+                                     sen ? max(sen[krow] - kj + 1, 0) : 0x7fffffff);
   const int64_t krowoff = ((int64_t)bg * T + krow) * D;
   const bf16* qsrc = a.pro ? a.qh : a.q;
 
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
 
   const int kwg_last = min(kwg0 + kBNkv - 1, T - 1);
   const int q_begin = kwg0;
-  const int q_end = window > 0 ? min(T, kwg_last + window) : T;
+  const int q_end = min(window > 0 ? min(T, kwg_last + window) : T, sen ? sen[kwg_last] + 1 : T);
   const int qt0 = q_begin / kBMt, qt1 = (q_end - 1) / kBMt;
   const int nq = qt1 - qt0 + 1;
   const int nit = G * nq;
@@ -365,6 +376,9 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
 
   const bool wave_active = kw0 < T;
   const int kw_last = min(kw0 + 31, T - 1);
+  // Earliest and latest run end among the wave's keys (packed rows; run ends grow with the
+  // token index).
+  const int e_lo = sen ? sen[min(kw0, T - 1)] : T, e_hi = sen ? sen[kw_last] : T;
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
@@ -373,9 +387,10 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
     const int hh = it / nq;
     const int q0 = (qt0 + it - hh * nq) * kBMt;
     const int q_last = min(q0 + kBMt - 1, T - 1);
-    const bool skip = !wave_active || q_last < kw0 || (window > 0 && q0 > kw_last + window - 1);
+    const bool skip = !wave_active || q_last < kw0 || q0 > e_hi ||
+                      (window > 0 && q0 > kw_last + window - 1);
     if (skip) return;
-    const bool need_mask = (q0 < kw_last) || (q0 + kBMt > T) ||
+    const bool need_mask = (q0 < kw_last) || (q0 + kBMt > T) || q_last > e_lo ||
                            (window > 0 && q_last - kw0 >= window);
     // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
     const int kd = q0 + 4 * gl - kj;
@@ -495,6 +510,8 @@ BwdArgs make_args(const BwdParams& p, int D) {
   a.lse = p.lse;
   a.Dvec = p.Dvec;
   a.L2 = p.L2;
+  a.seg_start = p.seg_start;
+  a.seg_end = p.seg_end;
   a.dq = (bf16*)p.dq;
   a.dk = (bf16*)p.dk;
   a.dv = (bf16*)p.dv;

@@ -34,6 +34,7 @@ struct FwdArgs {
   bf16* o;
   float* lse;                // may be null (extend: no LSE output)
   const int32_t* cache_len;  // extend: rows already cached per sequence (null in training)
+  const int32_t* seg_start;  // packed rows: first index of each token's run, [B, T] (or null)
   int B, T, Hq, Hkv, window, nqt;
   int Tk;                    // rows per head of k/v (T in training, Lmax for a cache)
   float shift;  // fixed softmax shift (log2 units) when the score bound allows one
@@ -66,8 +67,10 @@ __device__ __forceinline__ void pv_block(f32x16 (&oacc)[D / 32], const bf16* sv,
 
 // MODE: score transform (kScore*); FIXED: fixed shift instead of a running maximum.
 // Three waves per SIMD for D <= 96 (registers and 52 KB of LDS per workgroup fit), else two.
-template <int D, int MODE, bool FIXED>
-__global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs a) {
+// PACKED: rows carry several runs (segment ids); a compile-time switch so the plain kernels
+// keep the window limit in a scalar register (the packed ones run two waves per SIMD).
+template <int D, int MODE, bool FIXED, bool PACKED>
+__global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int LD = D + 8;          // LDS row pitch (elements)
   constexpr int NS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension
@@ -107,6 +110,9 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   const int qrow = min(qi, nq - 1);
   const int window = a.window;
   const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
+  // Packed rows: this lane's query sees keys back to the start of its run only.
+  const int32_t* sst = PACKED ? a.seg_start + (int64_t)b * T : nullptr;
+  const unsigned lim = PACKED ? min(wlim, (unsigned)(qrow - sst[qrow] + 1)) : wlim;
 
   const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * Tk * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * Tk * D;
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   }
 
   const int k_end = min(nk, off + q0 + kBM);
-  const int k_begin = window > 0 ? max(0, off + q0 - window + 1) : 0;
+  const int k_begin = max(window > 0 ? max(0, off + q0 - window + 1) : 0, PACKED ? sst[q0] : 0);
   const int kt0 = k_begin / kBN, kt1 = (k_end - 1) / kBN;
 
   // Tile loads: rows past T read clamped, finite data whose scores the causal mask removes
@@ -152,16 +158,21 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   // Positions of the wave's first and last existing query.
   const bool wave_active = qw0 < nq;
   const int pw0 = off + qw0, pw_last = off + min(qw0 + 31, nq - 1);
+  // Earliest and latest run start among the wave's queries (packed rows; run starts grow
+  // with the token index).
+  const int s_lo = PACKED ? sst[min(qw0, nq - 1)] : 0;
+  const int s_hi = PACKED ? sst[min(qw0 + 31, nq - 1)] : 0;
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
   // One key tile against this wave's 32 queries, operands in (sk, sv).
   auto run = [&](int kt, const bf16* sk, const bf16* sv) {
     const int k0 = kt * kBN;
-    const bool skip = !wave_active || k0 > pw_last ||
+    const bool skip = !wave_active || k0 > pw_last || k0 + kBN - 1 < s_lo ||
                       (window > 0 && k0 + kBN - 1 < pw0 - window + 1);
     if (!skip) {
-      const bool need_mask = (k0 + kBN - 1 > pw0) || (window > 0 && k0 < pw_last - window + 1);
+      const bool need_mask = (k0 + kBN - 1 > pw0) || k0 < s_hi ||
+                             (window > 0 && k0 < pw_last - window + 1);
       // position - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
       const int qd = off + qi - k0 - 4 * gl;
       if constexpr (FIXED) {
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
             for (int r = 0; r < 16; ++r) {
               float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
               if constexpr (MASKED)
-                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
+                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
               sacc[kb][r] = exp2_fast(y);
             }
             pb[kb][0] = pack8(sacc[kb], 0);
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256, D <= 96 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
             for (int r = 0; r < 16; ++r) {
               float y = score_y<MODE, false>(sacc[kb][r], a.sc, 0.f, nullptr);
               if constexpr (decltype(masked)::value)
-                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), wlim) ? y : kNegBig;
+                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
               sacc[kb][r] = y;
               mx = fmaxf(mx, y);
             }
@@ -402,6 +413,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
   }
 }
 
+// Launch the plain or the packed-rows instantiation.
+template <void (*PLAIN)(FwdArgs), void (*PACKED)(FwdArgs)>
+void launch_k(dim3 grid, hipStream_t s, const FwdArgs& a) {
+  if (a.seg_start)
+    hipLaunchKernelGGL(PACKED, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(PLAIN, grid, dim3(256), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   FwdArgs a;
@@ -411,6 +431,7 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   a.o = (bf16*)p.o;
   a.lse = p.lse;
   a.cache_len = p.cache_len;
+  a.seg_start = p.seg_start;
   a.B = p.B;
   a.T = p.T;
   a.Tk = p.cache_len ? p.Lmax : p.T;
@@ -426,15 +447,20 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   static const char* names[4] = {"fwd_bf16_d32", "fwd_bf16_d64", "fwd_bf16_d96", "fwd_bf16_d128"};
   TraceScope t(names[D / 32 - 1], s);
   if (ss.mode == kScoreScale && ss.fixed_shift)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreScale, true>), grid, dim3(256), 0, s, a);
+    launch_k<fwd_bf16_kernel<D, kScoreScale, true, false>,
+             fwd_bf16_kernel<D, kScoreScale, true, true>>(grid, s, a);
   else if (ss.mode == kScoreScale)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreScale, false>), grid, dim3(256), 0, s, a);
+    launch_k<fwd_bf16_kernel<D, kScoreScale, false, false>,
+             fwd_bf16_kernel<D, kScoreScale, false, true>>(grid, s, a);
   else if (ss.mode == kScoreCapPoly5 && ss.fixed_shift)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapPoly5, true>), grid, dim3(256), 0, s, a);
+    launch_k<fwd_bf16_kernel<D, kScoreCapPoly5, true, false>,
+             fwd_bf16_kernel<D, kScoreCapPoly5, true, true>>(grid, s, a);
   else if (ss.mode == kScoreCapPoly && ss.fixed_shift)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapPoly, true>), grid, dim3(256), 0, s, a);
+    launch_k<fwd_bf16_kernel<D, kScoreCapPoly, true, false>,
+             fwd_bf16_kernel<D, kScoreCapPoly, true, true>>(grid, s, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kScoreCapExp, false>), grid, dim3(256), 0, s, a);
+    launch_k<fwd_bf16_kernel<D, kScoreCapExp, false, false>,
+             fwd_bf16_kernel<D, kScoreCapExp, false, true>>(grid, s, a);
   return hipGetLastError();
 }
 

@@ -83,6 +83,9 @@ inline RowPrologue make_row_prologue(int rope, float rope_base, int qk_norm, flo
 
 // ---- row passes (rowops.hip) -------------------------------------------------------------
 // y = N(R(x)) for rows of length D; row r sits at position r % T.  elt = 2 (bf16) or 4 (f32).
+// segment ids [B, T] -> first / last token index of every token's run (packed rows).
+hipError_t launch_segment_bounds(const int32_t* ids, int32_t* start, int32_t* end, int B, int T,
+                                 hipStream_t s);
 // k_new/v_new [B, Hkv, S, D] -> cache rows cache_len[b] + i (RoPE at that position, QK-norm);
 // rows at or past Lmax are not written.
 hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
@@ -108,6 +111,8 @@ struct FwdParams {
   // (already holding the new keys), query i sits at position cache_len[b] + i.
   const int32_t* cache_len = nullptr;
   int Lmax = 0;
+  // Packed rows: first token index of every token's run, [B, T] (null: one run per row).
+  const int32_t* seg_start = nullptr;
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);  // q, k already prologued
@@ -133,6 +138,9 @@ struct BwdParams {
   float rope_base;
   int qk_norm;
   float eps;
+  // Packed rows: first / last token index of every token's run, [B, T] (null: one run).
+  const int32_t* seg_start = nullptr;
+  const int32_t* seg_end = nullptr;
 };
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t s);

@@ -193,6 +193,57 @@ hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
   return hipGetLastError();
 }
 
+// Packed rows (nanoGPT-JAX 181M model card, SFT notes: rows packed with segment ids): a
+// segment is a maximal run of equal ids.  For every token, start = index of the first token
+// of its run and end = index of the last; attention stays inside [start, end].  One
+// workgroup per row: each thread scans a contiguous span, then the spans' boundaries are
+// combined with a prefix maximum (starts) and a suffix minimum (ends) over the threads.
+__global__ __launch_bounds__(1024) void segment_bounds_kernel(const int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ st,
+                                                             int32_t* __restrict__ en, int T) {
+  __shared__ int smax[1024], smin[1024];
+  const int64_t base = (int64_t)blockIdx.x * T;
+  const int t = threadIdx.x;
+  const int span = (T + 1023) / 1024;
+  const int a = min(t * span, T), z = min(a + span, T);
+  int lmax = -1, lmin = 0x7fffffff;
+  for (int i = a; i < z; ++i) {
+    const int id = ids[base + i];
+    if (i == 0 || id != ids[base + i - 1]) lmax = i;                      // a run starts at i
+    if (lmin == 0x7fffffff && (i == T - 1 || id != ids[base + i + 1])) lmin = i;  // first run end
+  }
+  smax[t] = lmax;
+  smin[t] = lmin;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive prefix max / suffix min
+    const int vmax = t >= off ? smax[t - off] : -1;
+    const int vmin = t + off < 1024 ? smin[t + off] : 0x7fffffff;
+    __syncthreads();
+    smax[t] = max(smax[t], vmax);
+    smin[t] = min(smin[t], vmin);
+    __syncthreads();
+  }
+  int run = t > 0 ? smax[t - 1] : -1;
+  for (int i = a; i < z; ++i) {
+    if (i == 0 || ids[base + i] != ids[base + i - 1]) run = i;
+    st[base + i] = run;
+  }
+  int runm = t < 1023 ? smin[t + 1] : 0x7fffffff;
+  for (int i = z - 1; i >= a; --i) {
+    if (i == T - 1 || ids[base + i] != ids[base + i + 1]) runm = i;
+    en[base + i] = runm;
+  }
+}
+
+hipError_t launch_segment_bounds(const int32_t* ids, int32_t* start, int32_t* end, int B, int T,
+                                 hipStream_t s) {
+  if (B <= 0 || T <= 0) return hipSuccess;
+  TraceScope t("segment_bounds", s);
+  hipLaunchKernelGGL(segment_bounds_kernel, dim3((unsigned)B), dim3(1024), 0, s, ids, start, end,
+                     T);
+  return hipGetLastError();
+}
+
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

@@ -51,6 +51,8 @@ class Workload:
     backward: bool = True
     decode: bool = False         # single-token KV-cache decode instead of fwd/bwd
     len_lo: int = 0              # decode: cache lengths ~ U{len_lo .. T}
+    seg_lo: int = 0              # packed rows: run lengths ~ U{seg_lo .. seg_hi} (0 = unpacked)
+    seg_hi: int = 0
     new_tokens: int = 0          # extend: tokens appended per sequence (cache lengths ~
                                  # U{len_lo .. T - new_tokens}, T = allocated rows)
     seed: int = SEED_BASE
@@ -82,6 +84,10 @@ WORKLOADS = {
     "gqa181m_decode": Workload("gqa181m_decode", B=64, T=2048, Hq=8, Hkv=4, D=96, softcap=50.0,
                                rope=True, backward=False, decode=True, len_lo=256,
                                seed=SEED_BASE + 4),
+    # SFT-style packed rows on the 181M shapes: each row holds sequences of U{64..1024} tokens.
+    "gqa181m_sft_packed": Workload("gqa181m_sft_packed", B=16, T=2048, Hq=8, Hkv=4, D=96,
+                                   softcap=50.0, rope=True, qk_norm=True, seg_lo=64, seg_hi=1024,
+                                   seed=SEED_BASE + 9),
     # A multi-token step on the decode caches: 128 new tokens per sequence (chunked prefill or
     # speculative verification) against cache lengths U{256..1920}.
     "gqa181m_extend": Workload("gqa181m_extend", B=64, T=2048, Hq=8, Hkv=4, D=96, softcap=50.0,
@@ -131,6 +137,30 @@ def make_decode_inputs(w: Workload, seed: int | None = None):
     kc = _normal(rng, (w.B, w.Hkv, w.T, w.D), True)
     vc = _normal(rng, (w.B, w.Hkv, w.T, w.D), True)
     return q, kc, vc, cache_len
+
+
+def make_segment_ids(w: Workload, seed: int | None = None) -> np.ndarray:
+    """int32 [B, T] segment ids: each row is cut into runs of U{seg_lo .. seg_hi} tokens (the
+    last run takes what is left), numbered 0, 1, 2, ... within the row."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 1000)
+    ids = np.empty((w.B, w.T), dtype=np.int32)
+    for b in range(w.B):
+        a, n = 0, 0
+        while a < w.T:
+            L = int(rng.integers(w.seg_lo, w.seg_hi, endpoint=True))
+            ids[b, a:a + L] = n
+            a, n = a + L, n + 1
+    return ids
+
+
+def packed_flops(w: Workload, ids) -> float:
+    """14 d flops per visible pair; runs of length n have n (n + 1) / 2 pairs per head."""
+    pairs = 0
+    for row in np.asarray(ids):
+        cuts = np.flatnonzero(np.diff(row)) + 1
+        for n in np.diff(np.concatenate([[0], cuts, [len(row)]])):
+            pairs += int(n) * (int(n) + 1) // 2
+    return 14.0 * w.D * w.Hq * pairs
 
 
 def make_extend_inputs(w: Workload, seed: int | None = None):

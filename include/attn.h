@@ -103,6 +103,10 @@ typedef struct {
 size_t attn_fwd_workspace_bytes(const attn_cfg* cfg);
 size_t attn_bwd_workspace_bytes(const attn_cfg* cfg);
 size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg);
+/* The same for attn_fwd_packed / attn_bwd_packed (the plain figure plus 8 * B * T bytes, each
+ * region 256-byte aligned). */
+size_t attn_fwd_packed_workspace_bytes(const attn_cfg* cfg);
+size_t attn_bwd_packed_workspace_bytes(const attn_cfg* cfg);
 
 /* Host-only validation of a configuration; the status attn_fwd would return for it
  * (before pointer and workspace checks).  for_backward = 1 applies the backward's rules. */
@@ -133,6 +137,25 @@ int attn_fwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, v
 int attn_bwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, const void* o,
              const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
              size_t ws_bytes, void* stream);
+
+/*
+ * attn_fwd_packed, attn_bwd_packed -- attn_fwd / attn_bwd for rows that pack several
+ * sequences (the nanoGPT-JAX 181M model card's SFT data: rows packed with segment ids).
+ *   segment_ids [B, T] device, int32 -- a segment is a maximal run of equal ids in a row;
+ *             token i attends to key j iff j <= i, j is in i's run (and i - j < W with a
+ *             window).  Any id values are allowed; equal ids in separate runs are separate.
+ * Every other argument is as for attn_fwd / attn_bwd (the backward consumes the packed
+ * forward's o and lse); the workspaces are attn_fwd_packed_workspace_bytes /
+ * attn_bwd_packed_workspace_bytes.  RoPE positions stay the row positions: scores see RoPE
+ * only through position differences, so restarting them per run would change nothing.
+ * Packed rows are bfloat16 only.  segment_ids may be NULL only when there is nothing to do.
+ */
+int attn_fwd_packed(const attn_cfg* cfg, const void* q, const void* k, const void* v,
+                    const int32_t* segment_ids, void* o, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+int attn_bwd_packed(const attn_cfg* cfg, const void* q, const void* k, const void* v,
+                    const void* o, const void* dO, const float* lse, const int32_t* segment_ids,
+                    void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * attn_decode -- one new query per sequence against its KV cache (split-K over the cache

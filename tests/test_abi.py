@@ -85,6 +85,32 @@ def test_workspace_sizes(L):
     assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 16 * 98 * 4
 
 
+def test_packed_workspace_and_validation(L):
+    c = cfg(B=16, T=2048)
+    rows = 16 * 2048
+    extra = 2 * ((rows * 4 + 255) // 256 * 256)
+    assert L.attn_fwd_packed_workspace_bytes(ctypes.byref(c)) == \
+        L.attn_fwd_workspace_bytes(ctypes.byref(c)) + extra
+    assert L.attn_bwd_packed_workspace_bytes(ctypes.byref(c)) == \
+        L.attn_bwd_workspace_bytes(ctypes.byref(c)) + extra
+    fake, null, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0), ctypes.c_void_p(0)
+    small = cfg()
+    # segment ids are required when there is work
+    assert L.attn_fwd_packed(ctypes.byref(small), fake, fake, fake, null, fake, fake, fake,
+                             1 << 40, s) == -1
+    assert L.attn_bwd_packed(ctypes.byref(small), fake, fake, fake, fake, fake, fake, null, fake,
+                             fake, fake, fake, 1 << 40, s) == -1
+    f32 = cfg(dtype=bd.ATTN_F32)
+    assert L.attn_fwd_packed(ctypes.byref(f32), fake, fake, fake, fake, fake, fake, fake,
+                             1 << 40, s) == -2
+    # the packed workspace is checked against the packed figure
+    need = L.attn_fwd_packed_workspace_bytes(ctypes.byref(small))
+    assert L.attn_fwd_packed(ctypes.byref(small), fake, fake, fake, fake, fake, fake, fake,
+                             need - 1, s) == -3
+    empty = cfg(T=0)
+    assert L.attn_fwd_packed(ctypes.byref(empty), null, null, null, null, null, null, null, 0, s) == 0
+
+
 def test_decode_config_validation(L):
     o = bd.AttnOptions(softcap=50.0, rope=True)
     assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, 2048, o))) == 0

@@ -12,7 +12,8 @@ import pytest
 
 from causal_attention_02_amd import AttnOptions, attn_bwd, attn_decode, attn_extend, attn_fwd
 from causal_attention_02_amd.inputs import (WORKLOADS, Workload, make_decode_inputs,
-                                            make_extend_inputs, make_train_inputs, round_to_bf16)
+                                            make_extend_inputs, make_segment_ids,
+                                            make_train_inputs, round_to_bf16)
 from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
                     rms_normalize, rope_rotate)
 from tests.util import (TOL_F32_MAXABS, TOL_GRAD, TOL_LSE_BF16, TOL_O, max_abs, rel_l2, to_dev,
@@ -274,6 +275,66 @@ def test_decode_with_qk_norm():
 # --------------------------------------------------------------------------------------------
 # Error paths through the binding on a GPU (nothing is launched)
 # --------------------------------------------------------------------------------------------
+# --------------------------------------------------------------------------------------------
+# packed rows: segment ids keep attention inside each run
+# --------------------------------------------------------------------------------------------
+def ids_from_runs(runs_per_row):
+    rows = []
+    for runs in runs_per_row:
+        rows.append(np.concatenate([np.full(n, i % 4, dtype=np.int32) for i, n in enumerate(runs)]))
+    return np.stack(rows)
+
+
+PACKED_CASES = [
+    (Workload("packed181", B=2, T=300, Hq=8, Hkv=4, D=96, softcap=50.0, rope=True, qk_norm=True),
+     [[37, 1, 130, 64, 68], [300]]),
+    (Workload("packed_window", B=2, T=333, Hq=6, Hkv=3, D=128, window=100, rope=True, qk_norm=True),
+     [[200, 133], [1] * 333]),
+    (Workload("packed_d64", B=3, T=129, Hq=4, Hkv=4, D=64, rope=True, softcap=20.0),
+     [[64, 65], [5] * 25 + [4], [129]]),
+    (Workload("packed_d32", B=2, T=257, Hq=4, Hkv=2, D=32, qk_norm=True), [[128, 129], [2, 255]]),
+]
+
+
+def gpu_fwd_bwd_packed(w, q, k, v, dO, ids):
+    import torch
+    tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+    tids = torch.from_numpy(ids).to("cuda")
+    o, lse = attn_fwd(tq, tk, tv, opts_of(w), segment_ids=tids)
+    g = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w), segment_ids=tids)
+    torch.cuda.synchronize()
+    return (to_host(o), to_host(lse)) + tuple(to_host(x) for x in g)
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=[c[0].name for c in PACKED_CASES])
+def test_packed_rows(case):
+    w, runs = case
+    ids = ids_from_runs(runs)
+    _say(f"case {w.name}: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} W={w.window} runs={runs}")
+    q, k, v, dO = make_train_inputs(w)
+    got = gpu_fwd_bwd_packed(w, q, k, v, dO, ids)
+    kw = dict(oracle_kw(w), segment_ids=ids)
+    check_bf16(w, got, attention_forward(q, k, v, **kw), attention_backward(q, k, v, dO, **kw), w.name)
+
+
+def test_packed_full_size_sampled():
+    w = WORKLOADS["gqa181m_sft_packed"]
+    ids = make_segment_ids(w)
+    _say(f"case {w.name} full size: B={w.B} T={w.T} runs of {w.seg_lo}..{w.seg_hi}")
+    q, k, v, dO = make_train_inputs(w)
+    got = gpu_fwd_bwd_packed(w, q, k, v, dO, ids)
+    G = w.Hq // w.Hkv
+    for b, g in [(0, 0), (w.B // 2, w.Hkv // 2), (w.B - 1, w.Hkv - 1)]:
+        hs = slice(g * G, (g + 1) * G)
+        qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
+        kw = dict(oracle_kw(w), segment_ids=ids[b:b + 1])
+        ref_f = attention_forward(qs, ks, vs, **kw)
+        ref_b = attention_backward(qs, ks, vs, dos, **kw)
+        sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
+              got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
+        check_bf16(w, sl, ref_f, ref_b, f"{w.name}[b={b},g={g}]")
+
+
 # --------------------------------------------------------------------------------------------
 # extend: S new tokens against a KV cache (append, then attend with the offset mask)
 # --------------------------------------------------------------------------------------------
