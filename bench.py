@@ -88,11 +88,14 @@ def main():
               "multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
+    import ctypes
+
     import torch
 
     from causal_attention_02_amd import binding as bd
     from causal_attention_02_amd.inputs import (WORKLOADS, decode_bytes, make_decode_inputs,
                                                 extend_flops, make_extend_inputs,
+                                                make_segment_ids, packed_flops,
                                                 make_train_inputs, train_flops, visible_pairs)
 
     if not torch.cuda.is_available():
@@ -113,8 +116,9 @@ def main():
     # ------------------------------------------------------------------------------------
     # fwd + bwd
     # ------------------------------------------------------------------------------------
-    def train_case(w, steps, warmup, trace=False):
+    def train_case(w, steps, warmup, trace=False, ids=None):
         q, k, v, dO = make_train_inputs(w)
+        tids = None if ids is None else torch.from_numpy(ids).to(dev)
         tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(dO)
         del q, k, v, dO
         o = torch.empty_like(tq)
@@ -123,14 +127,20 @@ def main():
         opts = opts_of(w)
         B, Hq, T, D = tq.shape
         Hkv = tk.shape[1]
-        wsf = torch.empty(max(bd.fwd_workspace_bytes(B, T, Hq, Hkv, D, opts), 1), dtype=torch.uint8,
-                          device=dev)
-        wsb = torch.empty(max(bd.bwd_workspace_bytes(B, T, Hq, Hkv, D, opts), 1), dtype=torch.uint8,
-                          device=dev)
+        cfg = bd.make_cfg(B, T, Hq, Hkv, D, opts, bd.ATTN_BF16)
+        if tids is None:
+            nf = bd.lib().attn_fwd_workspace_bytes(ctypes.byref(cfg))
+            nb = bd.lib().attn_bwd_workspace_bytes(ctypes.byref(cfg))
+        else:
+            nf = bd.lib().attn_fwd_packed_workspace_bytes(ctypes.byref(cfg))
+            nb = bd.lib().attn_bwd_packed_workspace_bytes(ctypes.byref(cfg))
+        wsf = torch.empty(max(int(nf), 1), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(max(int(nb), 1), dtype=torch.uint8, device=dev)
 
         def step():
-            bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf)
-            bd.attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb)
+            bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf, segment_ids=tids)
+            bd.attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb,
+                        segment_ids=tids)
 
         for _ in range(warmup):
             step()
@@ -190,6 +200,15 @@ def main():
             extra[name] = dict(ms_per_step=ms2, ms_median=float(np.median(per2)), tflops=tf2,
                                pct_peak=100 * tf2 / PEAK_BF16_TFLOPS)
             log(f"[bench] {name}: {ms2:.3f} ms/step  {tf2:.1f} TFLOP/s")
+        # SFT-style packed rows (segment ids) on the 181M shapes.
+        wp = WORKLOADS["gqa181m_sft_packed"]
+        ids = make_segment_ids(wp)
+        log(f"[bench] fwd+bwd {wp.name}")
+        msp, perp, _ = train_case(wp, max(args.steps // 2, 3), 2, ids=ids)
+        tfp = packed_flops(wp, ids) / (msp * 1e-3) / 1e12
+        extra[wp.name] = dict(ms_per_step=msp, ms_median=float(np.median(perp)), tflops=tfp,
+                              pct_peak=100 * tfp / PEAK_BF16_TFLOPS)
+        log(f"[bench] {wp.name}: {msp:.3f} ms/step  {tfp:.1f} TFLOP/s")
         torch.cuda.empty_cache()
 
     if args.copy_mib > 0:
@@ -219,7 +238,6 @@ def main():
         od = torch.empty_like(tq)
         opts = opts_of(wd)
         cfg = bd.make_decode_cfg(wd.B, wd.Hq, wd.Hkv, wd.D, wd.T, opts)
-        import ctypes
         wsd = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg))),
                           dtype=torch.uint8, device=dev)
         for i in range(10):
