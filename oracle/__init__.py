@@ -4,6 +4,9 @@ from .attn_ref import (  # noqa: F401
     attention_decode,
     attention_extend,
     attention_forward,
+    dropout_fields,
+    dropout_keep,
+    dropout_threshold,
     rms_normalize,
     rope_rotate,
     rope_unrotate,

@@ -51,8 +51,21 @@ project's design notes):
   is stored, and rows that would land at or past Lmax are not stored (their queries
   return zero rows).
 
+* Attention dropout ("GPT pretraining" page, section "Multihead Attention": dropout on the
+  attention weights after the softmax, before they multiply V; rate 0.1 in the page's GPT
+  configuration): inverted dropout, as the page's dropout layer does -- a weight is kept
+  with probability 1 - p and then scaled by 1 / (1 - p), or set to zero.  The keep
+  decision for query i and key j of head (b, h) compares a 16-bit random field with
+  t = round(65536 p); the rate actually applied is t / 65536 and the scale is
+  65536 / (65536 - t).  The fields come from the counter-based generator Philox4x64-10
+  (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011)
+  with key (seed, 0) and counter (floor(j / 16), i, b * H + h, offset): field j mod 16 of
+  that 256-bit block, counting 16-bit fields from the low end of output word 0.  The
+  log-sum-exp returned by the forward stays that of the softmax before dropout.
+
 Everything is computed densely per (batch, head) in float64 with numpy; there is
-no tiling, fusion or reordering beyond the definitions above.
+no tiling, fusion or reordering beyond the definitions above.  numpy's own Philox
+bit generator supplies the Philox blocks.
 """
 from __future__ import annotations
 
@@ -68,6 +81,9 @@ __all__ = [
     "attention_backward",
     "attention_decode",
     "attention_extend",
+    "dropout_threshold",
+    "dropout_fields",
+    "dropout_keep",
 ]
 
 
@@ -190,6 +206,61 @@ def _softmax_rows(s, allowed):
     return e / l, (m + np.log(l))[..., 0]
 
 
+# --------------------------------------------------------------------------------------
+# Attention dropout ("GPT pretraining" page, "Multihead Attention")
+# --------------------------------------------------------------------------------------
+def dropout_threshold(p: float):
+    """(t, scale): the 16-bit threshold t = round(65536 p) and the kept-weight scale 65536 / (65536 - t).
+
+    A weight is kept iff its random field is >= t, so the rate applied is t / 65536.
+    Requires 0 <= p and t < 65536.
+    """
+    p = float(p)
+    if not p >= 0.0:
+        raise ValueError("dropout rate must be >= 0")
+    t = int(np.floor(p * 65536.0 + 0.5))
+    if t >= 65536:
+        raise ValueError("dropout rate rounds to 1")
+    return t, 65536.0 / (65536 - t)
+
+
+def dropout_fields(b: int, h: int, H: int, i: int, T: int, seed: int, offset: int) -> np.ndarray:
+    """The 16-bit random fields of keys 0..T-1 for query i of head (b, h), as uint16 [T].
+
+    Block n (keys 16 n .. 16 n + 15) is Philox4x64-10 with key (seed, 0) applied to the
+    counter (n, i, b H + h, offset); key 16 n + 4 w + f takes bits 16 f .. 16 f + 15 of the
+    block's output word w.  numpy's Philox encrypts the counter after incrementing it, so it
+    is started one below the first block's counter.
+    """
+    nb = (T + 15) // 16
+    c = (int(i) << 64) | (int(b * H + h) << 128) | (int(offset) << 192)
+    gen = np.random.Philox(key=np.array([int(seed), 0], dtype=np.uint64),
+                           counter=(c - 1) % (1 << 256))
+    words = gen.random_raw(4 * nb).astype(np.uint64)  # block n: words 4 n .. 4 n + 3
+    shifts = np.arange(0, 64, 16, dtype=np.uint64)
+    fields = (words[:, None] >> shifts[None, :]) & np.uint64(0xFFFF)
+    return fields.reshape(-1)[:T].astype(np.uint16)
+
+
+def dropout_keep(B: int, H: int, T: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """Keep mask [B, H, T, T] (bool): entry (b, h, i, j) is True iff dropout keeps weight P_ij."""
+    t, _ = dropout_threshold(p)
+    keep = np.empty((B, H, T, T), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(T):
+                keep[b, h, i] = dropout_fields(b, h, H, i, T, seed, offset) >= t
+    return keep
+
+
+def _dropout_factor(keep, p, b, h):
+    """Per-entry factor keep / (1 - rate) for head (b, h), or None without dropout."""
+    if keep is None:
+        return None
+    _, scale = dropout_threshold(p)
+    return np.where(keep[b, h], scale, 0.0)
+
+
 def _check_shapes(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, T, d]")
@@ -203,12 +274,15 @@ def _check_shapes(q, k, v):
 
 
 def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
-                      rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None):
+                      rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None,
+                      dropout_p=0.0, dropout_keep=None):
     """Causal attention forward for q [B,Hq,T,d], k/v [B,Hkv,T,d]; returns (O [B,Hq,T,d], LSE [B,Hq,T]).
 
     Per (b, h):  q^ = prologue(q), k^ = prologue(k);  S = scale * q^ k^T;  S <- c tanh(S / c)
     if capped;  masked entries -> -inf;  P = row softmax(S);  O = P V;  LSE = ln sum_j exp(S_ij).
     segment_ids [B, T] (optional): packed rows, see the module notes.
+    dropout_keep [B, Hq, T, T] (optional, with rate dropout_p): O = (P * Z) V with
+    Z = keep / (1 - rate); the LSE is unchanged.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -227,17 +301,21 @@ def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
             qh, _ = _prologue(q[b, h], pos, rope, rope_base, qk_norm, norm_eps)
             _, s = _scores(qh, khat[g], scale, softcap)
             P, lse = _softmax_rows(s, allowed)
-            O[b, h] = P @ v[b, g]
+            Z = _dropout_factor(dropout_keep, dropout_p, b, h)
+            O[b, h] = (P if Z is None else P * Z) @ v[b, g]
             LSE[b, h] = lse
     return O, LSE
 
 
 def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=False,
-                       rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None):
+                       rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None,
+                       dropout_p=0.0, dropout_keep=None):
     """Analytic gradients (dQ, dK, dV) of <O, dO> with respect to the RAW q, k, v.
 
     Per (b, h) with g = kv head of h:
       dV_g += P^T dO;  dP = dO V_g^T;  D_i = sum_d dO_i O_i;  dS = P * (dP - D);
+    with dropout (Z = keep / (1 - rate), O = (P * Z) V):  dV_g += (P * Z)^T dO and
+    dP = Z * (dO V_g^T), D unchanged (it equals sum_j P_ij dP_ij either way);
       dS_pre = dS * (1 - tanh(S_pre / c)^2) if capped;
       dq^ = scale dS_pre k^;  dk^_g += scale dS_pre^T q^;
     then each of dq^, dk^ goes back through RMSNorm and RoPE.
@@ -265,9 +343,13 @@ def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=F
             khat = kpro[g][0]
             s_pre, s = _scores(qhat, khat, scale, softcap)
             P, _ = _softmax_rows(s, allowed)
-            O = P @ v[b, g]
-            dV[b, g] += P.T @ dO[b, h]
+            Z = _dropout_factor(dropout_keep, dropout_p, b, h)
+            Pz = P if Z is None else P * Z
+            O = Pz @ v[b, g]
+            dV[b, g] += Pz.T @ dO[b, h]
             dP = dO[b, h] @ v[b, g].T
+            if Z is not None:
+                dP = dP * Z
             D = np.sum(dO[b, h] * O, axis=-1, keepdims=True)
             dS = P * (dP - D)
             if softcap > 0:

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
-                    rms_normalize, rope_rotate, rope_unrotate, segment_starts, visible_mask)
+                    dropout_fields, dropout_keep, dropout_threshold, rms_normalize, rope_rotate,
+                    rope_unrotate, segment_starts, visible_mask)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -608,3 +609,171 @@ def test_workload_shapes_match_pages():
     assert (w.B, w.T, w.Hq, w.Hkv, w.D) == (g2["batch_size"], g2["context_length"], heads, heads,
                                             d_model // heads)
     assert all(dm // h == 64 for dm, h in g2["sizes"])
+
+
+# ------------------------------------------------------------------------------------
+# Attention dropout ("GPT pretraining" page, "Multihead Attention").
+# ------------------------------------------------------------------------------------
+_M64 = (1 << 64) - 1
+
+
+def philox4x64_10(ctr, key):
+    """Philox4x64-10 from its published definition (Salmon et al., SC 2011), scalar Python.
+
+    Round: (hi0, lo0) = M0 * x0, (hi1, lo1) = M1 * x2 (128-bit products);
+    x <- (hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0); the key is bumped by the Weyl
+    constants between rounds.
+    """
+    m0, m1 = 0xD2E7470EE14C6C93, 0xCA5A826395121157
+    w0, w1 = 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B
+    x = [int(c) & _M64 for c in ctr]
+    k0, k1 = int(key[0]) & _M64, int(key[1]) & _M64
+    for r in range(10):
+        if r:
+            k0, k1 = (k0 + w0) & _M64, (k1 + w1) & _M64
+        p0, p1 = m0 * x[0], m1 * x[2]
+        x = [(p1 >> 64) ^ x[1] ^ k0, p1 & _M64, (p0 >> 64) ^ x[3] ^ k1, p0 & _M64]
+    return x
+
+
+def test_philox_definition_matches_numpy():
+    # The scalar definition above against numpy's Philox bit generator (which encrypts the
+    # counter after incrementing it).
+    rng = np.random.default_rng(40)
+    for n in range(50):
+        ctr = [int(c) for c in rng.integers(0, 2 ** 63, 4, dtype=np.int64)]
+        key = [int(c) for c in rng.integers(0, 2 ** 63, 2, dtype=np.int64)]
+        if n < 3:
+            ctr = [n, 0, 0, 0]
+        c = sum(v << (64 * i) for i, v in enumerate(ctr))
+        gen = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=(c - 1) % (1 << 256))
+        assert [int(w) for w in gen.random_raw(4)] == philox4x64_10(ctr, key)
+
+
+def test_dropout_fields_follow_the_counter_layout():
+    # Field of key j for query i of head (b, h): block (j // 16, i, b H + h, offset) under key
+    # (seed, 0), word (j % 16) // 4, bits 16 (j % 4) ...
+    for (b, h, H, i, T, seed, offset) in [(0, 0, 1, 0, 5, 0, 0), (1, 2, 3, 7, 40, 42, 5),
+                                          (3, 11, 12, 255, 256, 2 ** 63 + 9, 2 ** 40)]:
+        got = dropout_fields(b, h, H, i, T, seed, offset)
+        want = []
+        for j in range(T):
+            blk = philox4x64_10([j // 16, i, b * H + h, offset], [seed, 0])
+            want.append((blk[(j % 16) // 4] >> (16 * (j % 4))) & 0xFFFF)
+        assert got.tolist() == want
+
+
+def test_dropout_threshold_values():
+    assert dropout_threshold(0.0) == (0, 1.0)
+    assert dropout_threshold(0.5) == (32768, 2.0)
+    t, sc = dropout_threshold(0.1)
+    assert t == 6554 and sc == 65536.0 / (65536 - 6554)
+    assert dropout_threshold(1.0 - 2.0 ** -16)[0] == 65535
+    for bad in (-0.1, 1.0, 0.99999999):
+        with pytest.raises(ValueError):
+            dropout_threshold(bad)
+
+
+def test_dropout_keep_rate_and_independence():
+    B, H, T = 2, 3, 96
+    for p in (0.1, 0.5):
+        keep = dropout_keep(B, H, T, p, seed=42, offset=0)
+        t, _ = dropout_threshold(p)
+        q = t / 65536.0
+        n = keep.size
+        assert abs((1.0 - keep.mean()) - q) < 5 * math.sqrt(q * (1 - q) / n)
+        # Another seed, another offset, another head: agreement as for independent draws.
+        for other in (dropout_keep(B, H, T, p, seed=43, offset=0),
+                      dropout_keep(B, H, T, p, seed=42, offset=1)):
+            agree = np.mean(keep == other)
+            e = q * q + (1 - q) * (1 - q)
+            assert abs(agree - e) < 5 * math.sqrt(e * (1 - e) / n)
+        assert not np.array_equal(keep[0, 0], keep[0, 1])
+        assert not np.array_equal(keep[0, 0], keep[1, 0])
+    assert dropout_keep(1, 2, 33, 0.0, seed=1).all()
+
+
+def brute_force_dropout_forward(q, k, v, keep, scale_d):
+    """Plain causal attention with the weights multiplied by keep * scale_d; scalar loops."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    O = np.zeros((B, Hq, T, d))
+    for b, h, i in itertools.product(range(B), range(Hq), range(T)):
+        g = h * Hkv // Hq
+        s = [sum(q[b, h, i, c] * k[b, g, j, c] for c in range(d)) / math.sqrt(d) for j in range(i + 1)]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = sum(w)
+        for j in range(i + 1):
+            if keep[b, h, i, j]:
+                O[b, h, i] += (w[j] / tot) * scale_d * v[b, g, j]
+    return O
+
+
+def test_dropout_forward_matches_brute_force():
+    rng = np.random.default_rng(41)
+    for (Hq, Hkv, T, d, p) in [(2, 1, 7, 4, 0.3), (3, 3, 18, 2, 0.1), (4, 2, 33, 8, 0.5)]:
+        q, k, v = rnd(rng, 2, Hq, T, d), rnd(rng, 2, Hkv, T, d), rnd(rng, 2, Hkv, T, d)
+        keep = dropout_keep(2, Hq, T, p, seed=7, offset=3)
+        O, L = attention_forward(q, k, v, dropout_p=p, dropout_keep=keep)
+        _, sc = dropout_threshold(p)
+        np.testing.assert_allclose(O, brute_force_dropout_forward(q, k, v, keep, sc), atol=1e-12)
+        np.testing.assert_allclose(L, attention_forward(q, k, v)[1], atol=0)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_dropout_special_cases(flags):
+    rng = np.random.default_rng(42)
+    q, k, v, dO = rnd(rng, 1, 2, 9, 4), rnd(rng, 1, 1, 9, 4), rnd(rng, 1, 1, 9, 4), rnd(rng, 1, 2, 9, 4)
+    plain = attention_forward(q, k, v, **flags)
+    # Rate 0 keeps everything at scale 1.
+    keep0 = dropout_keep(1, 2, 9, 0.0, seed=3)
+    np.testing.assert_array_equal(attention_forward(q, k, v, dropout_p=0.0, dropout_keep=keep0,
+                                                    **flags)[0], plain[0])
+    # Everything kept at rate 1/2: twice the output, twice the gradients of <O, dO>.
+    allk = np.ones((1, 2, 9, 9), dtype=bool)
+    np.testing.assert_allclose(attention_forward(q, k, v, dropout_p=0.5, dropout_keep=allk,
+                                                 **flags)[0], 2 * plain[0], atol=1e-14)
+    for a, b in zip(attention_backward(q, k, v, dO, dropout_p=0.5, dropout_keep=allk, **flags),
+                    attention_backward(q, k, v, dO, **flags)):
+        np.testing.assert_allclose(a, 2 * b, atol=1e-12)
+    # Nothing kept: zero output and zero gradients.
+    nok = np.zeros((1, 2, 9, 9), dtype=bool)
+    assert not attention_forward(q, k, v, dropout_p=0.5, dropout_keep=nok, **flags)[0].any()
+    for a in attention_backward(q, k, v, dO, dropout_p=0.5, dropout_keep=nok, **flags):
+        np.testing.assert_allclose(a, 0, atol=1e-15)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS[:3])
+def test_dropout_gradients_match_finite_differences(flags):
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, T, d, p = 1, 2, 1, 7, 4, 0.3
+    q, k, v, dO = rnd(rng, B, Hq, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hkv, T, d), rnd(rng, B, Hq, T, d)
+    keep = dropout_keep(B, Hq, T, p, seed=11, offset=0)
+    kw = dict(dropout_p=p, dropout_keep=keep, **flags)
+    grads = attention_backward(q, k, v, dO, **kw)
+    f = lambda qq, kk, vv: float(np.sum(attention_forward(qq, kk, vv, **kw)[0] * dO))
+    eps = 1e-6
+    for which, x in enumerate((q, k, v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(grads[which], num, rtol=0, atol=2e-7)
+
+
+def test_dropout_is_unbiased():
+    # Inverted dropout: the mean output over independent masks tends to the plain output.
+    rng = np.random.default_rng(44)
+    q, k, v = rnd(rng, 1, 1, 6, 4), rnd(rng, 1, 1, 6, 4), rnd(rng, 1, 1, 6, 4)
+    plain = attention_forward(q, k, v)[0]
+    p, n = 0.3, 600
+    outs = np.stack([attention_forward(q, k, v, dropout_p=p,
+                                       dropout_keep=dropout_keep(1, 1, 6, p, seed=s))[0]
+                     for s in range(n)])
+    se = outs.std(axis=0) / math.sqrt(n)
+    assert np.all(np.abs(outs.mean(axis=0) - plain) <= 5 * se + 1e-12)
