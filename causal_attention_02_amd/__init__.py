@@ -9,9 +9,11 @@ from .binding import (  # noqa: F401
     AttnOptions,
     attn_bwd,
     attn_decode,
+    attn_dropout_mask,
     attn_extend,
     attn_fwd,
     bwd_workspace_bytes,
+    dropout_mask_bytes,
     fwd_workspace_bytes,
     lib,
     trace_enable,

@@ -22,7 +22,8 @@ EXPORTED = [
     "attn_fwd_packed_workspace_bytes", "attn_bwd_packed_workspace_bytes",
     "attn_check_cfg", "attn_check_decode_cfg", "attn_check_extend_cfg", "attn_fwd", "attn_bwd",
     "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
-    "attn_trace_enable", "attn_trace_read",
+    "attn_trace_enable", "attn_trace_read", "attn_dropout_mask_bytes", "attn_dropout_mask",
+    "attn_fwd_dropout", "attn_bwd_dropout",
 ]
 
 
@@ -99,6 +100,16 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_packed.restype = ctypes.c_int
         L.attn_bwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_bwd_packed.restype = ctypes.c_int
+        f32, u64 = ctypes.c_float, ctypes.c_uint64
+        L.attn_dropout_mask_bytes.argtypes = [cfgp]
+        L.attn_dropout_mask_bytes.restype = sz
+        L.attn_dropout_mask.argtypes = [cfgp, f32, u64, u64, vp, sz, vp]
+        L.attn_dropout_mask.restype = ctypes.c_int
+        L.attn_fwd_dropout.argtypes = [cfgp, vp, vp, vp, f32, vp, sz, vp, vp, vp, sz, vp]
+        L.attn_fwd_dropout.restype = ctypes.c_int
+        L.attn_bwd_dropout.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp, vp, vp,
+                                       sz, vp]
+        L.attn_bwd_dropout.restype = ctypes.c_int
         L.attn_decode.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_decode.restype = ctypes.c_int
         L.attn_extend.argtypes = [ecfgp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -207,12 +218,42 @@ def bwd_workspace_bytes(B, T, Hq, Hkv, D, opts: AttnOptions) -> int:
     return int(lib().attn_bwd_workspace_bytes(ctypes.byref(make_cfg(B, T, Hq, Hkv, D, opts, ATTN_BF16))))
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def dropout_mask_bytes(B, T, Hq, Hkv, D, opts: AttnOptions | None = None) -> int:
+    cfg = make_cfg(B, T, Hq, Hkv, D, opts or AttnOptions(), ATTN_BF16)
+    return int(lib().attn_dropout_mask_bytes(ctypes.byref(cfg)))
+
+
+def attn_dropout_mask(q, k, p: float, seed: int, offset: int = 0, opts: AttnOptions | None = None,
+                      *, out=None, stream=None):
+    """Keep mask (uint8 buffer of dropout_mask_bytes) for dropout rate p on the attention weights
+    of q [B,Hq,T,D] against k [B,Hkv,T,D]; pass it with the same p to attn_fwd / attn_bwd."""
+    torch = _torch()
+    opts = opts or AttnOptions()
+    B, Hq, T, D = q.shape
+    cfg = make_cfg(B, T, Hq, k.shape[1], D, opts, ATTN_BF16)
+    _check(lib().attn_check_cfg(ctypes.byref(cfg), 0), "attn_dropout_mask")
+    n = int(lib().attn_dropout_mask_bytes(ctypes.byref(cfg)))
+    m = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device) if out is None else out
+    if _nbytes(m) < n or not m.is_cuda or not m.is_contiguous():
+        raise ValueError(f"dropout mask: need a contiguous GPU buffer of {n} bytes")
+    st = lib().attn_dropout_mask(ctypes.byref(cfg), ctypes.c_float(p), ctypes.c_uint64(seed),
+                                 ctypes.c_uint64(offset), _ptr(m), ctypes.c_size_t(_nbytes(m)),
+                                 _stream(stream))
+    _check(st, "attn_dropout_mask")
+    return m
+
+
 def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, workspace=None,
-             stream=None, segment_ids=None):
+             stream=None, segment_ids=None, dropout_p=0.0, dropout_mask=None):
     """Forward: q [B,Hq,T,D], k/v [B,Hkv,T,D] (bf16 or fp32) -> (o, lse fp32 [B,Hq,T]).
 
     segment_ids (int32 [B,T], optional): packed rows; attention stays inside each run of equal
-    ids (bf16 only)."""
+    ids (bf16 only).  dropout_mask (from attn_dropout_mask with rate dropout_p, optional):
+    dropout on the attention weights (bf16 only)."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, T, D = q.shape
@@ -228,6 +269,16 @@ def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, wo
     cfg = make_cfg(B, T, Hq, Hkv, D, opts, dt)
     st = lib().attn_check_cfg(ctypes.byref(cfg), 0)
     _check(st, "attn_fwd")
+    if dropout_mask is not None:
+        if segment_ids is not None:
+            raise ValueError("dropout with segment ids is not supported")
+        ws = _workspace(int(lib().attn_fwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+        st = lib().attn_fwd_dropout(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                    ctypes.c_float(dropout_p), _ptr(dropout_mask),
+                                    ctypes.c_size_t(_nbytes(dropout_mask)), _ptr(o), _ptr(lse_t),
+                                    _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream(stream))
+        _check(st, "attn_fwd_dropout")
+        return o, lse_t
     if segment_ids is not None:
         _need(segment_ids, (B, T), torch.int32, "segment_ids")
         ws = _workspace(int(lib().attn_fwd_packed_workspace_bytes(ctypes.byref(cfg))), q.device,
@@ -247,9 +298,9 @@ def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, wo
 
 
 def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, segment_ids=None):
+             workspace=None, stream=None, segment_ids=None, dropout_p=0.0, dropout_mask=None):
     """Backward (bf16): returns (dq, dk, dv) with respect to the raw q, k, v (packed rows with
-    segment_ids as in attn_fwd)."""
+    segment_ids, dropout with the forward's dropout_mask and dropout_p, as in attn_fwd)."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, T, D = q.shape
@@ -267,6 +318,17 @@ def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, d
     _need(dv, v.shape, bf, "dv")
     cfg = make_cfg(B, T, Hq, Hkv, D, opts, ATTN_BF16)
     _check(lib().attn_check_cfg(ctypes.byref(cfg), 1), "attn_bwd")
+    if dropout_mask is not None:
+        if segment_ids is not None:
+            raise ValueError("dropout with segment ids is not supported")
+        ws = _workspace(int(lib().attn_bwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+        st = lib().attn_bwd_dropout(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                                    _ptr(lse), ctypes.c_float(dropout_p), _ptr(dropout_mask),
+                                    ctypes.c_size_t(_nbytes(dropout_mask)), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(ws), ctypes.c_size_t(_nbytes(ws)),
+                                    _stream(stream))
+        _check(st, "attn_bwd_dropout")
+        return dq, dk, dv
     if segment_ids is not None:
         _need(segment_ids, (B, T), torch.int32, "segment_ids")
         ws = _workspace(int(lib().attn_bwd_packed_workspace_bytes(ctypes.byref(cfg))), q.device,

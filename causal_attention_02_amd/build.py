@@ -19,7 +19,7 @@ LIB_NAME = "libcausal_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.hip", "rowops.hip", "fwd.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["attn_api.hip", "rowops.hip", "fwd.hip", "bwd.hip", "decode.hip", "dropout.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -173,6 +173,23 @@ size_t bwd_ws(const attn_cfg* c) {
 // Packed rows: run starts and ends, [B, T] int32 each.
 size_t seg_ws(const attn_cfg* c) { return 2 * align_up((size_t)c->B * c->T * 4); }
 
+// Dropout keep masks: row layout then column layout, B * Hq * T rows of dropout_pitch(T)
+// words each.
+size_t drop_half(const attn_cfg* c) {
+  return align_up((size_t)c->B * c->Hq * c->T * dropout_pitch(c->T) * 4);
+}
+size_t drop_bytes(const attn_cfg* c) { return 2 * drop_half(c); }
+
+// 16-bit keep threshold round(65536 p) and the kept-weight scale, or false if p is out of range.
+bool drop_params(float p, uint32_t* thr, float* scale) {
+  if (!(p >= 0.f) || !isfinite(p)) return false;
+  const double t = floor((double)p * 65536.0 + 0.5);
+  if (t >= 65536.0) return false;
+  *thr = (uint32_t)t;
+  *scale = (float)(65536.0 / (65536.0 - t));
+  return true;
+}
+
 size_t dec_ws(const attn_decode_cfg* c) {
   return align_up((size_t)c->B * c->Hq * decode_nsplit(c) * (c->D + 2) * 4);
 }
@@ -216,12 +233,14 @@ size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg) {
 
 // Forward and backward bodies; `ids` (segment ids [B, T], or null) selects packed rows, whose
 // run starts (and ends) go to a region after the plain workspace.
+// Dropout: `drop` points to a keep-mask buffer (row layout, then column layout) and dscale
+// is the kept-weight scale.
 static int fwd_impl(const attn_cfg* c, const void* q, const void* k, const void* v,
                     const int32_t* ids, void* o, float* lse, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    void* stream, const void* drop = nullptr, float dscale = 1.f) {
   int st = check_cfg(c, 0);
   if (st != ATTN_OK) return st;
-  if (ids && c->dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if ((ids || drop) && c->dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (c->B == 0 || c->T == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
   const size_t need = fwd_ws(c) + (ids ? seg_ws(c) : 0);
@@ -232,6 +251,8 @@ static int fwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
   FwdParams p{q, k, v, o, lse, c->B, c->T, c->Hq, c->Hkv, c->D, c->window,
               eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
               c->norm_eps};
+  p.drop_rows = (const uint32_t*)drop;
+  p.drop_scale = dscale;
   hipError_t e = hipSuccess;
   if (ids) {
     int32_t* sst = (int32_t*)((char*)ws + fwd_ws(c));
@@ -265,7 +286,8 @@ static int fwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
 
 static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void* v,
                     const void* o, const void* dO, const float* lse, const int32_t* ids,
-                    void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+                    void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
+                    const void* drop = nullptr, float dscale = 1.f) {
   int st = check_cfg(c, 1);
   if (st != ATTN_OK) return st;
   if (c->B == 0 || c->T == 0) return ATTN_OK;
@@ -294,6 +316,11 @@ static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
   BwdParams p{q, k, kh, qh, v, o, dO, lse, Dvec, L2, dq, dk, dv, c->B, c->T, c->Hq, c->Hkv, c->D,
               c->window, eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base,
               c->qk_norm, c->norm_eps};
+  if (drop) {
+    p.drop_rows = (const uint32_t*)drop;
+    p.drop_cols = (const uint32_t*)((const char*)drop + drop_half(c));
+    p.drop_scale = dscale;
+  }
   if (ids && e == hipSuccess) {
     int32_t* sst = (int32_t*)((char*)ws + bwd_ws(c));
     int32_t* sen = (int32_t*)((char*)sst + align_up((size_t)c->B * c->T * 4));
@@ -329,6 +356,53 @@ int attn_bwd_packed(const attn_cfg* c, const void* q, const void* k, const void*
                     void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
   if (!segment_ids && c && c->B > 0 && c->T > 0) return ATTN_EINVAL;
   return bwd_impl(c, q, k, v, o, dO, lse, segment_ids, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+size_t attn_dropout_mask_bytes(const attn_cfg* cfg) {
+  return check_cfg(cfg, 0) == ATTN_OK ? drop_bytes(cfg) : 0;
+}
+
+int attn_dropout_mask(const attn_cfg* c, float p, uint64_t seed, uint64_t offset, void* mask,
+                      size_t mask_bytes, void* stream) {
+  int st = check_cfg(c, 0);
+  if (st != ATTN_OK) return st;
+  uint32_t thr;
+  float scale;
+  if (!drop_params(p, &thr, &scale)) return ATTN_EINVAL;
+  if (c->B == 0 || c->T == 0) return ATTN_OK;
+  if (!mask || mask_bytes < drop_bytes(c)) return ATTN_EINVAL;
+  uint32_t* rows = (uint32_t*)mask;
+  uint32_t* cols = (uint32_t*)((char*)mask + drop_half(c));
+  return launch_status(launch_dropout_mask(rows, cols, c->B, c->Hq, c->T, c->window, thr, seed,
+                                           offset, (hipStream_t)stream));
+}
+
+int attn_fwd_dropout(const attn_cfg* c, const void* q, const void* k, const void* v, float p,
+                     const void* mask, size_t mask_bytes, void* o, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_cfg(c, 0);
+  if (st != ATTN_OK) return st;
+  uint32_t thr;
+  float scale;
+  if (!drop_params(p, &thr, &scale)) return ATTN_EINVAL;
+  if (c->dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (c->B == 0 || c->T == 0) return ATTN_OK;
+  if (!mask || mask_bytes < drop_bytes(c)) return ATTN_EINVAL;
+  return fwd_impl(c, q, k, v, nullptr, o, lse, ws, ws_bytes, stream, mask, scale);
+}
+
+int attn_bwd_dropout(const attn_cfg* c, const void* q, const void* k, const void* v,
+                     const void* o, const void* dO, const float* lse, float p, const void* mask,
+                     size_t mask_bytes, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int st = check_cfg(c, 1);
+  if (st != ATTN_OK) return st;
+  uint32_t thr;
+  float scale;
+  if (!drop_params(p, &thr, &scale)) return ATTN_EINVAL;
+  if (c->B == 0 || c->T == 0) return ATTN_OK;
+  if (!mask || mask_bytes < drop_bytes(c)) return ATTN_EINVAL;
+  return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream, mask, scale);
 }
 
 int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, const void* v_cache,

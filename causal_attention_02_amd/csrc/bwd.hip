@@ -24,6 +24,11 @@
 //    dV^T += dO^T P and dK^T += q^T dS need for their B operands; the transposed A operands
 //    come from ds_read_b64_tr_b16.  dK and dV of a KV head are summed over its query group
 //    inside the workgroup.
+//
+// Dropout on the weights (O = (P * Z) V, Z = keep / (1 - rate)): dV = (P * Z)^T dO and
+// dS = P * (Z * (dO V^T) - D) with the same D.  The DROP instantiations stage each tile's
+// keep words in LDS beside it (row layout for dq, column layout for dkdv), start dP at 0
+// instead of -D, and scale dV once at the end.
 #include <type_traits>
 
 #include "device_common.h"
@@ -46,6 +51,10 @@ struct BwdArgs {
   float* L2;  // LSE * log2(e) per query row (written by dq for dkdv)
   const int32_t* seg_start;  // packed rows: first / last index of each token's run, [B, T]
   const int32_t* seg_end;    // (null: one run per row)
+  const uint32_t* drop_rows; // dropout keep masks, row and column layouts (or null)
+  const uint32_t* drop_cols;
+  int drop_pitch;
+  float drop_scale;          // kept-weight scale 1 / (1 - rate)
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -100,7 +109,7 @@ constexpr int kBMq = 128;  // queries per dq workgroup
 constexpr int kBNk = 64;   // keys per dq tile
 
 // Two waves per SIMD where the registers fit (all D <= 96; D = 128 without a soft-cap).
-template <int D, int MODE>
+template <int D, int MODE, bool DROP>
 __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
@@ -111,6 +120,9 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
   __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
+  // Dropout keep words of the tile's two 32-key blocks for the 128 queries: [block][query].
+  __shared__ __attribute__((aligned(16))) uint32_t sM0[DROP ? 2 * kBMq : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t sM1[DROP ? 2 * kBMq : 1];
 
   const int T = a.T;
   const int nbh = a.B * a.Hq;
@@ -178,6 +190,13 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   auto dma = [&](int kt, int buf) {
     tdma.copy(buf ? sK1 : sK0, kbase, kt * kBNk, T, w);
     tdma.copy(buf ? sV1 : sV0, vbase, kt * kBNk, T, w);
+    if constexpr (DROP) {
+      // Wave w: keep word of block (w & 1) for queries q0 + 64 (w >> 1) + lane.
+      const int row = min(q0 + 64 * (w >> 1) + l, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          a.drop_rows + ((int64_t)bh * T + row) * a.drop_pitch + 2 * kt + (w & 1),
+          (buf ? sM1 : sM0) + (w & 1) * kBMq + 64 * (w >> 1), 4, 0, 0);
+    }
   };
 
   f32x16 dqacc[NDB];
@@ -196,11 +215,16 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   // One key tile: S^T = K q^T and dP^T = V dO^T for both 32-key blocks (dP^T accumulates on
   // top of -D_i, so it comes out as dP - D), then per half block dS and dQ^T += K^T dS^T.
   // The phase fences keep one phase's registers live at a time (two waves share a SIMD).
-  auto run = [&](int kt, const bf16* sk, const bf16* sv) {
+  auto run = [&](int kt, const bf16* sk, const bf16* sv, const uint32_t* sm) {
     const int k0 = kt * kBNk;
     const bool skip = !wave_active || k0 > qw_last || k0 + kBNk - 1 < s_lo ||
                       (window > 0 && k0 + kBNk - 1 < qw0 - window + 1);
     if (skip) return;
+    uint32_t mw[2] = {0u, 0u};
+    if constexpr (DROP) {
+      mw[0] = sm[qi - q0] >> (4 * gl);
+      mw[1] = sm[kBMq + qi - q0] >> (4 * gl);
+    }
     const bool need_mask = (k0 + kBNk - 1 > qw0) || k0 < s_hi ||
                            (window > 0 && k0 < qw_last - window + 1);
     // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[kb][r] = 0.f;
-        pacc[kb][r] = -Di;
+        pacc[kb][r] = DROP ? 0.f : -Di;
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -238,7 +262,10 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
               y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
             float p = exp2_fast(y);
             if constexpr (MODE != kScoreScale) p *= gf;
-            sacc[kb][r] = p * pacc[kb][r];
+            if constexpr (DROP)
+              sacc[kb][r] = p * fmaf(keep_only(a.drop_scale, mw[kb], r), pacc[kb][r], -Di);
+            else
+              sacc[kb][r] = p * pacc[kb][r];
           }
         };
         if (need_mask)
@@ -267,12 +294,12 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   __syncthreads();
   for (int kt = kt0; kt <= kt1; kt += 2) {
     if (kt + 1 <= kt1) dma(kt + 1, 1);
-    run(kt, sK0, sV0);
+    run(kt, sK0, sV0, sM0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 1 > kt1) break;
     if (kt + 2 <= kt1) dma(kt + 2, 0);
-    run(kt + 1, sK1, sV1);
+    run(kt + 1, sK1, sV1, sM1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -287,8 +314,10 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
 constexpr int kBNkv = 128;  // keys per dkdv workgroup
 constexpr int kBMt = 64;    // queries per dkdv tile
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdArgs a) {
+// Two waves per SIMD for D <= 64, and for D = 96 without dropout (its keep words and -D
+// values no longer fit the 256 registers two waves allow); one otherwise.
+template <int D, int MODE, bool DROP>
+__global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
@@ -300,6 +329,9 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
   __shared__ __attribute__((aligned(16))) bf16 sO1[TILE];
   __shared__ __attribute__((aligned(16))) float sL[2][kBMt];  // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBMt];  // -D, D = rowsum(dO * O)
+  // Dropout keep words of the tile's two 32-query blocks for the 128 keys: [block][key].
+  __shared__ __attribute__((aligned(16))) uint32_t sM0[DROP ? 2 * kBNkv : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t sM1[DROP ? 2 * kBNkv : 1];
 
   const int T = a.T;
   const int nbg = a.B * a.Hkv;
@@ -363,6 +395,13 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
     const int64_t qc = hbase + min(q0 + l, T - 1);
     if (w == 2) __builtin_amdgcn_global_load_lds(a.L2 + qc, &sL[buf][0], 4, 0, 0);
     if (w == 3) __builtin_amdgcn_global_load_lds(a.Dvec + qc, &sD[buf][0], 4, 0, 0);
+    if constexpr (DROP) {
+      // Wave w: keep word of query block (w & 1) for keys kwg0 + 64 (w >> 1) + lane.
+      const int key = min(kwg0 + 64 * (w >> 1) + l, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          a.drop_cols + (hbase + key) * a.drop_pitch + q0 / 32 + (w & 1),
+          (buf ? sM1 : sM0) + (w & 1) * kBNkv + 64 * (w >> 1), 4, 0, 0);
+    }
   };
 
   f32x16 dvacc[NDB], dkacc[NDB];
@@ -382,8 +421,9 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  // One q tile against this wave's 32 keys, operands in (sq, so, sl, sd).
-  auto step = [&](int it, const bf16* sq, const bf16* so, const float* sl, const float* sd) {
+  // One q tile against this wave's 32 keys, operands in (sq, so, sl, sd), keep words in sm.
+  auto step = [&](int it, const bf16* sq, const bf16* so, const float* sl, const float* sd,
+                  const uint32_t* sm) {
     const int hh = it / nq;
     const int q0 = (qt0 + it - hh * nq) * kBMt;
     const int q_last = min(q0 + kBMt - 1, T - 1);
@@ -400,13 +440,20 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
       // top of -D (element r belongs to query offset 8 (r / 4) + r % 4 of the block), so it
       // comes out as dP - D.
       f32x16 sacc, pacc;
+      uint32_t mw = 0u;
+      if constexpr (DROP) {
+        mw = sm[qb * kBNkv + kj - kwg0] >> (4 * gl);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 nd = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 8 * i);
-        pacc[4 * i] = nd.x;
-        pacc[4 * i + 1] = nd.y;
-        pacc[4 * i + 2] = nd.z;
-        pacc[4 * i + 3] = nd.w;
+        for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 nd = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 8 * i);
+          pacc[4 * i] = nd.x;
+          pacc[4 * i + 1] = nd.y;
+          pacc[4 * i + 2] = nd.z;
+          pacc[4 * i + 3] = nd.w;
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
@@ -427,6 +474,11 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
       for (int t = 0; t < 2; ++t) {
         const float4 lq[2] = {*reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t),
                               *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t + 8)};
+        float4 nq[2];  // -D of the half's queries (dropout: dP starts at 0)
+        if constexpr (DROP) {
+          nq[0] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t);
+          nq[1] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t + 8);
+        }
         auto grads = [&](auto masked) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -437,9 +489,17 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
             if constexpr (decltype(masked)::value)
               y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
             const float p = exp2_fast(y);
-            float ds = p * pacc[r];
+            float ds;
+            if constexpr (DROP) {
+              const float4 n4 = nq[e >> 2];
+              const float nd = (e & 3) == 0 ? n4.x : (e & 3) == 1 ? n4.y : (e & 3) == 2 ? n4.z : n4.w;
+              ds = p * fmaf(keep_only(a.drop_scale, mw, r), pacc[r], nd);
+              sacc[r] = keep_only(p, mw, r);  // dV takes the kept weights; scaled at the end
+            } else {
+              ds = p * pacc[r];
+              sacc[r] = p;
+            }
             if constexpr (MODE != kScoreScale) ds *= gf;
-            sacc[r] = p;
             pacc[r] = ds;
           }
         };
@@ -473,12 +533,12 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
   __syncthreads();
   for (int it = 0; it < nit; it += 2) {
     if (it + 1 < nit) dma(it + 1, 1);
-    step(it, sQ0, sO0, sL[0], sD[0]);
+    step(it, sQ0, sO0, sL[0], sD[0], sM0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (it + 1 >= nit) break;
     if (it + 2 < nit) dma(it + 2, 0);
-    step(it + 1, sQ1, sO1, sL[1], sD[1]);
+    step(it + 1, sQ1, sO1, sL[1], sD[1], sM1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -492,7 +552,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void bwd_dkdv_kernel(BwdAr
       for (int i4 = 0; i4 < 4; ++i4) {
         float v4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = dvacc[db][4 * i4 + j];
+        for (int j = 0; j < 4; ++j) v4[j] = dvacc[db][4 * i4 + j] * (DROP ? a.drop_scale : 1.f);
         store4(a.dv + krowoff + 32 * db + 8 * i4 + 4 * gl, v4);
       }
   }
@@ -512,6 +572,10 @@ BwdArgs make_args(const BwdParams& p, int D) {
   a.L2 = p.L2;
   a.seg_start = p.seg_start;
   a.seg_end = p.seg_end;
+  a.drop_rows = p.drop_rows;
+  a.drop_cols = p.drop_cols;
+  a.drop_pitch = dropout_pitch(p.T);
+  a.drop_scale = p.drop_scale;
   a.dq = (bf16*)p.dq;
   a.dk = (bf16*)p.dk;
   a.dv = (bf16*)p.dv;
@@ -536,14 +600,25 @@ hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.ntiles * p.B * p.Hq));
   static const char* names[4] = {"bwd_dq_d32", "bwd_dq_d64", "bwd_dq_d96", "bwd_dq_d128"};
   TraceScope t(names[D / 32 - 1], s);
-  if (mode == kScoreScale)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreScale>), grid, dim3(256), 0, s, a);
-  else if (mode == kScoreCapPoly5)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly5>), grid, dim3(256), 0, s, a);
-  else if (mode == kScoreCapPoly)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapExp>), grid, dim3(256), 0, s, a);
+  if (a.drop_rows) {
+    if (mode == kScoreScale)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreScale, true>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly5)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly5, true>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapExp, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (mode == kScoreScale)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreScale, false>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly5)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly5, false>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapPoly, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, kScoreCapExp, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -555,14 +630,25 @@ hipError_t launch_dkdv_d(const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.ntiles * p.B * p.Hkv));
   static const char* names[4] = {"bwd_dkdv_d32", "bwd_dkdv_d64", "bwd_dkdv_d96", "bwd_dkdv_d128"};
   TraceScope t(names[D / 32 - 1], s);
-  if (mode == kScoreScale)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale>), grid, dim3(256), 0, s, a);
-  else if (mode == kScoreCapPoly5)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5>), grid, dim3(256), 0, s, a);
-  else if (mode == kScoreCapPoly)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp>), grid, dim3(256), 0, s, a);
+  if (a.drop_cols) {
+    if (mode == kScoreScale)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale, true>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly5)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5, true>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (mode == kScoreScale)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale, false>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly5)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5, false>), grid, dim3(256), 0, s, a);
+    else if (mode == kScoreCapPoly)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -54,6 +54,34 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
   return r;
 }
 
+// ---- dropout keep bits -----------------------------------------------------------------
+// A lane's 16 accumulator elements of a 32-wide block sit at offsets 8 (r / 4) + r % 4 + 4 gl
+// of the block; `mw` is the block's keep word shifted right by 4 gl, so element r's bit is
+// keep_bit(r).
+__device__ __forceinline__ constexpr int keep_bit(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// All ones if bit `bit` of mw is set, else zero (v_bfe_i32).
+__device__ __forceinline__ uint32_t keep_all(uint32_t mw, int bit) {
+  return (uint32_t)((int32_t)(mw << (31 - bit)) >> 31);
+}
+
+// x where element r is kept, +0 where it is dropped.
+__device__ __forceinline__ float keep_only(float x, uint32_t mw, int r) {
+  return __uint_as_float(__float_as_uint(x) & keep_all(mw, keep_bit(r)));
+}
+
+// Zero the dropped weights of a packed half block (elements 8 h .. 8 h + 7, two per dword).
+__device__ __forceinline__ bf16x8 keep_packed(bf16x8 v, uint32_t mw, int h) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int bit = keep_bit(8 * h + 2 * d);  // the pair's second element is bit + 1
+    u[d] &= (keep_all(mw, bit) & 0xFFFFu) | (keep_all(mw, bit + 1) & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 // Sum of the 8 bf16 values with fp32 accumulation (v_dot2_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v) {
   const bf16x2 one = {(bf16)1.f, (bf16)1.f};

@@ -35,6 +35,9 @@ struct FwdArgs {
   float* lse;                // may be null (extend: no LSE output)
   const int32_t* cache_len;  // extend: rows already cached per sequence (null in training)
   const int32_t* seg_start;  // packed rows: first index of each token's run, [B, T] (or null)
+  const uint32_t* drop_rows; // dropout: row-layout keep mask [B, Hq, T, drop_pitch] (or null)
+  int drop_pitch;
+  float drop_scale;          // kept-weight scale 1 / (1 - rate)
   int B, T, Hq, Hkv, window, nqt;
   int Tk;                    // rows per head of k/v (T in training, Lmax for a cache)
   float shift;  // fixed softmax shift (log2 units) when the score bound allows one
@@ -65,12 +68,19 @@ __device__ __forceinline__ void pv_block(f32x16 (&oacc)[D / 32], const bf16* sv,
   }
 }
 
+// Kernel variants: plain rows; packed rows (segment ids); dropout on the weights.
+constexpr int kVarPlain = 0, kVarPacked = 1, kVarDrop = 2;
+
 // MODE: score transform (kScore*); FIXED: fixed shift instead of a running maximum.
 // Three waves per SIMD for D <= 96 (registers and 52 KB of LDS per workgroup fit), else two.
-// PACKED: rows carry several runs (segment ids); a compile-time switch so the plain kernels
-// keep the window limit in a scalar register (the packed ones run two waves per SIMD).
-template <int D, int MODE, bool FIXED, bool PACKED>
-__global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_kernel(FwdArgs a) {
+// VAR: kVarPacked -- rows carry several runs (segment ids); a compile-time switch so the plain
+// kernels keep the window limit in a scalar register.  kVarDrop -- dropout: the keep words of
+// each key tile are staged in LDS with the tile, the PV product takes the kept weights, the
+// row sum all of them, and the output is scaled by 1 / (1 - rate).  Both run two waves per SIMD.
+template <int D, int MODE, bool FIXED, int VAR>
+__global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr bool PACKED = VAR == kVarPacked;
+  constexpr bool DROP = VAR == kVarDrop;
   constexpr int LD = D + 8;          // LDS row pitch (elements)
   constexpr int NS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;        // 32-wide blocks of the head dimension
@@ -80,6 +90,10 @@ __global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_ke
   __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
   __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
+  // Dropout keep words of the tile's two 32-key blocks for the workgroup's 128 queries:
+  // [block][query].
+  __shared__ __attribute__((aligned(16))) uint32_t sM0[DROP ? 2 * kBM : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t sM1[DROP ? 2 * kBM : 1];
 
   const int T = a.T;  // query rows per head
   const int nbh = a.B * a.Hq;
@@ -146,6 +160,13 @@ __global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_ke
   auto dma = [&](int kt, int buf) {
     TileDma<D, 4>::copy_fresh(buf ? sK1 : sK0, kbase, kt * kBN, nk, w, l);
     TileDma<D, 4>::copy_fresh(buf ? sV1 : sV0, vbase, kt * kBN, nk, w, l);
+    if constexpr (DROP) {
+      // Wave w: keep word of block (w & 1) for queries q0 + 64 (w >> 1) + lane.
+      const int row = min(q0 + 64 * (w >> 1) + l, T - 1);
+      __builtin_amdgcn_global_load_lds(
+          a.drop_rows + ((int64_t)bh * T + row) * a.drop_pitch + 2 * kt + (w & 1),
+          (buf ? sM1 : sM0) + (w & 1) * kBM + 64 * (w >> 1), 4, 0, 0);
+    }
   };
 
   float m_run = FIXED ? a.shift : kNegBig, l_run = 0.f;
@@ -165,12 +186,17 @@ __global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_ke
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  // One key tile against this wave's 32 queries, operands in (sk, sv).
-  auto run = [&](int kt, const bf16* sk, const bf16* sv) {
+  // One key tile against this wave's 32 queries, operands in (sk, sv), keep words in sm.
+  auto run = [&](int kt, const bf16* sk, const bf16* sv, const uint32_t* sm) {
     const int k0 = kt * kBN;
     const bool skip = !wave_active || k0 > pw_last || k0 + kBN - 1 < s_lo ||
                       (window > 0 && k0 + kBN - 1 < pw0 - window + 1);
     if (!skip) {
+      uint32_t mw[2] = {0u, 0u};
+      if constexpr (DROP) {
+        mw[0] = sm[qi - q0] >> (4 * gl);
+        mw[1] = sm[kBM + qi - q0] >> (4 * gl);
+      }
       const bool need_mask = (k0 + kBN - 1 > pw0) || k0 < s_hi ||
                              (window > 0 && k0 < pw_last - window + 1);
       // position - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
@@ -208,11 +234,16 @@ __global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_ke
             // Row sum of the bf16-rounded weights, the values the PV product uses, so the
             // normalisation matches the numerator exactly (a single visible key returns V).
             l_run += sum_bf16x8(pb[kb][0]) + sum_bf16x8(pb[kb][1]);
+            if constexpr (DROP) {
+              pb[kb][0] = keep_packed(pb[kb][0], mw[kb], 0);
+              pb[kb][1] = keep_packed(pb[kb][1], mw[kb], 1);
+            }
             pv_block<D>(oacc, sv, kb, pb[kb], trow, tcol);
           }
           // Schedule: block 0 scores; block 1's K reads and score MFMAs under block 0's
           // weights; block 0's PV under block 1's weights; block 1's PV.
-          constexpr int VW = MASKED ? 26 : 22;  // VALU ops per interleave slot
+          // VALU ops per interleave slot (dropout adds 16 per packed half block).
+          constexpr int VW = (MASKED ? 26 : 22) + (DROP ? (32 + NS - 1) / NS : 0);
           __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
 #pragma unroll
@@ -275,8 +306,12 @@ __global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_ke
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(sacc[kb][r] - m_new);
-          const bf16x8 pb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
+          bf16x8 pb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
           l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
+          if constexpr (DROP) {
+            pb[0] = keep_packed(pb[0], mw[kb], 0);
+            pb[1] = keep_packed(pb[1], mw[kb], 1);
+          }
           pv_block<D>(oacc, sv, kb, pb, trow, tcol);
         }
       }
@@ -290,19 +325,19 @@ __global__ __launch_bounds__(256, (D <= 96 && !PACKED) ? 3 : 2) void fwd_bf16_ke
   __syncthreads();
   for (int kt = kt0; kt <= kt1; kt += 2) {
     if (kt + 1 <= kt1) dma(kt + 1, 1);
-    run(kt, sK0, sV0);
+    run(kt, sK0, sV0, sM0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 1 > kt1) break;
     if (kt + 2 <= kt1) dma(kt + 2, 0);
-    run(kt + 1, sK1, sV1);
+    run(kt + 1, sK1, sV1, sM1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   const float l_tot = pair_sum(l_run);
   if (qi < nq) {
-    const float inv = 1.f / l_tot;
+    const float inv = (DROP ? a.drop_scale : 1.f) / l_tot;
     bf16* op = a.o + ((int64_t)bh * T + qi) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -413,13 +448,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
   }
 }
 
-// Launch the plain or the packed-rows instantiation.
-template <void (*PLAIN)(FwdArgs), void (*PACKED)(FwdArgs)>
+// Launch the plain, packed-rows or dropout instantiation.
+template <int D, int MODE, bool FIXED>
 void launch_k(dim3 grid, hipStream_t s, const FwdArgs& a) {
   if (a.seg_start)
-    hipLaunchKernelGGL(PACKED, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, FIXED, kVarPacked>), grid, dim3(256), 0, s, a);
+  else if (a.drop_rows)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, FIXED, kVarDrop>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(PLAIN, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, FIXED, kVarPlain>), grid, dim3(256), 0, s, a);
 }
 
 template <int D>
@@ -432,6 +469,9 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   a.lse = p.lse;
   a.cache_len = p.cache_len;
   a.seg_start = p.seg_start;
+  a.drop_rows = p.drop_rows;
+  a.drop_pitch = dropout_pitch(p.T);
+  a.drop_scale = p.drop_scale;
   a.B = p.B;
   a.T = p.T;
   a.Tk = p.cache_len ? p.Lmax : p.T;
@@ -447,20 +487,15 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   static const char* names[4] = {"fwd_bf16_d32", "fwd_bf16_d64", "fwd_bf16_d96", "fwd_bf16_d128"};
   TraceScope t(names[D / 32 - 1], s);
   if (ss.mode == kScoreScale && ss.fixed_shift)
-    launch_k<fwd_bf16_kernel<D, kScoreScale, true, false>,
-             fwd_bf16_kernel<D, kScoreScale, true, true>>(grid, s, a);
+    launch_k<D, kScoreScale, true>(grid, s, a);
   else if (ss.mode == kScoreScale)
-    launch_k<fwd_bf16_kernel<D, kScoreScale, false, false>,
-             fwd_bf16_kernel<D, kScoreScale, false, true>>(grid, s, a);
+    launch_k<D, kScoreScale, false>(grid, s, a);
   else if (ss.mode == kScoreCapPoly5 && ss.fixed_shift)
-    launch_k<fwd_bf16_kernel<D, kScoreCapPoly5, true, false>,
-             fwd_bf16_kernel<D, kScoreCapPoly5, true, true>>(grid, s, a);
+    launch_k<D, kScoreCapPoly5, true>(grid, s, a);
   else if (ss.mode == kScoreCapPoly && ss.fixed_shift)
-    launch_k<fwd_bf16_kernel<D, kScoreCapPoly, true, false>,
-             fwd_bf16_kernel<D, kScoreCapPoly, true, true>>(grid, s, a);
+    launch_k<D, kScoreCapPoly, true>(grid, s, a);
   else
-    launch_k<fwd_bf16_kernel<D, kScoreCapExp, false, false>,
-             fwd_bf16_kernel<D, kScoreCapExp, false, true>>(grid, s, a);
+    launch_k<D, kScoreCapExp, false>(grid, s, a);
   return hipGetLastError();
 }
 

@@ -94,6 +94,16 @@ hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s);
 
+// ---- attention dropout (dropout.hip) ------------------------------------------------------
+// Keep masks, one bit per (query, key): 32-bit words, `dropout_pitch(T)` words per row (an even
+// count, so the attention kernels' 64-wide tiles always read whole word pairs).
+inline int dropout_pitch(int T) { return 2 * ((T + 63) / 64); }
+// rows [B, H, T, pitch]: bit c of word w of row i keeps (i, 32 w + c); cols [B, H, T, pitch]:
+// bit c of word w of row j keeps (32 w + c, j).  Only words of 32 x 32 tiles that meet the
+// causal / window band are written.  Keep iff the element's 16-bit Philox field >= thr.
+hipError_t launch_dropout_mask(uint32_t* rows, uint32_t* cols, int B, int H, int T, int window,
+                               uint32_t thr, uint64_t seed, uint64_t offset, hipStream_t s);
+
 // ---- forward (fwd.hip) -------------------------------------------------------------------
 struct FwdParams {
   const void* q;  // [B, Hq, T, D] raw q (bf16: RoPE/QK-norm applied in the kernel)
@@ -113,6 +123,9 @@ struct FwdParams {
   int Lmax = 0;
   // Packed rows: first token index of every token's run, [B, T] (null: one run per row).
   const int32_t* seg_start = nullptr;
+  // Dropout on the weights: row-layout keep mask (null: none) and the kept-weight scale.
+  const uint32_t* drop_rows = nullptr;
+  float drop_scale = 1.f;
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);  // q, k already prologued
@@ -141,6 +154,10 @@ struct BwdParams {
   // Packed rows: first / last token index of every token's run, [B, T] (null: one run).
   const int32_t* seg_start = nullptr;
   const int32_t* seg_end = nullptr;
+  // Dropout on the weights: keep masks in both layouts (null: none), kept-weight scale.
+  const uint32_t* drop_rows = nullptr;
+  const uint32_t* drop_cols = nullptr;
+  float drop_scale = 1.f;
 };
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t s);

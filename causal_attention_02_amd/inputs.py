@@ -55,6 +55,8 @@ class Workload:
     seg_hi: int = 0
     new_tokens: int = 0          # extend: tokens appended per sequence (cache lengths ~
                                  # U{len_lo .. T - new_tokens}, T = allocated rows)
+    dropout: float = 0.0         # dropout rate on the attention weights (0 = none); the keep
+                                 # mask is drawn with generator seed `seed`, offset 0
     seed: int = SEED_BASE
     note: str = field(default="", compare=False)
 
@@ -97,6 +99,9 @@ WORKLOADS = {
     # causal multi-head attention (learned position embeddings, no RoPE / QK-norm / cap).
     "gpt_pretrain_train": Workload("gpt_pretrain_train", B=128, T=256, Hq=12, Hkv=12, D=64,
                                    seed=SEED_BASE + 5),
+    # The same with the page's attention dropout (rate 0.1 on the weights) in training.
+    "gpt_pretrain_train_dropout": Workload("gpt_pretrain_train_dropout", B=128, T=256, Hq=12,
+                                           Hkv=12, D=64, dropout=0.1, seed=SEED_BASE + 10),
     # Instruction tuning on GPT-2 XL: 1600 dims over 25 heads -> d = 64, context 256, batch 8.
     "gpt2xl_instruct_train": Workload("gpt2xl_instruct_train", B=8, T=256, Hq=25, Hkv=25, D=64,
                                       seed=SEED_BASE + 6),

@@ -158,6 +158,41 @@ int attn_bwd_packed(const attn_cfg* cfg, const void* q, const void* k, const voi
                     void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Attention dropout -- the "GPT pretraining" page, section "Multihead Attention", applies
+ * dropout to the attention weights (after the softmax, before they multiply V; rate 0.1 in
+ * its GPT configuration).  Inverted dropout: a weight is kept with probability 1 - p and
+ * scaled by 1 / (1 - p), else zeroed.  The decision for query i, key j of head (b, h) takes
+ * the 16-bit field j mod 16 of the Philox4x64-10 block (Salmon et al., "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC 2011) for counter (floor(j / 16), i, b * Hq + h, offset)
+ * under key (seed, 0) -- field f is bits 16 (f mod 4) .. 16 (f mod 4) + 15 of output word
+ * f / 4 -- and keeps the weight iff field >= t = round(65536 p).  The rate applied is
+ * therefore t / 65536 and the scale 65536 / (65536 - t); p must satisfy 0 <= p and t < 65536.
+ *
+ * attn_dropout_mask_bytes -- size of the keep-mask buffer for cfg: two bit matrices of
+ *   B * Hq * T rows of 2 * ceil(T / 64) 32-bit words (one row-major over keys, one over
+ *   queries).  0 for an invalid configuration.
+ * attn_dropout_mask -- fill `mask` (device, >= attn_dropout_mask_bytes(cfg) bytes, owned by
+ *   the caller) with the keep bits of (p, seed, offset).  Only the words of 32 x 32 tiles that
+ *   meet the causal / window band are written; the rest of the buffer is left as it was.
+ *   A fresh (seed, offset) pair gives an independent mask.
+ * attn_fwd_dropout, attn_bwd_dropout -- attn_fwd / attn_bwd with the weights multiplied by
+ *   keep / (1 - rate): O = (P * Z) V, and the gradients of sum(O * dO) for that O.  `mask` is
+ *   the buffer attn_dropout_mask filled for the same cfg and p (the backward must see the
+ *   forward's mask); lse stays the log-sum-exp of the undropped scores.  Workspaces are those
+ *   of attn_fwd / attn_bwd.  bfloat16 only; one run per row (no segment ids).
+ */
+size_t attn_dropout_mask_bytes(const attn_cfg* cfg);
+int attn_dropout_mask(const attn_cfg* cfg, float p, uint64_t seed, uint64_t offset, void* mask,
+                      size_t mask_bytes, void* stream);
+int attn_fwd_dropout(const attn_cfg* cfg, const void* q, const void* k, const void* v, float p,
+                     const void* mask, size_t mask_bytes, void* o, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
+int attn_bwd_dropout(const attn_cfg* cfg, const void* q, const void* k, const void* v,
+                     const void* o, const void* dO, const float* lse, float p, const void* mask,
+                     size_t mask_bytes, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
  * attn_decode -- one new query per sequence against its KV cache (split-K over the cache
  * length, then an LSE-weighted merge of the chunks).  bfloat16 only.
  *   q         [B, Hq, D] device, bf16 -- raw (un-rotated) query of the newest token

@@ -111,6 +111,41 @@ def test_packed_workspace_and_validation(L):
     assert L.attn_fwd_packed(ctypes.byref(empty), null, null, null, null, null, null, null, 0, s) == 0
 
 
+def test_dropout_mask_bytes_and_validation(L):
+    c = cfg(B=16, T=2048)
+    pitch = 2 * ((2048 + 63) // 64)
+    half = (16 * 8 * 2048 * pitch * 4 + 255) // 256 * 256
+    assert L.attn_dropout_mask_bytes(ctypes.byref(c)) == 2 * half
+    odd = cfg(B=3, T=65)  # two 64-column word pairs per row
+    assert L.attn_dropout_mask_bytes(ctypes.byref(odd)) == \
+        2 * ((3 * 8 * 65 * 4 * 4 + 255) // 256 * 256)
+    fake, null, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0), ctypes.c_void_p(0)
+    small = cfg()
+    need = L.attn_dropout_mask_bytes(ctypes.byref(small))
+    u64 = ctypes.c_uint64
+    # rate out of range, missing or short mask: rejected before anything is enqueued
+    for p in (-0.1, 1.0, 1.0 - 2.0 ** -18, float("nan"), float("inf")):
+        assert L.attn_dropout_mask(ctypes.byref(small), p, u64(1), u64(0), fake, need, s) == -1
+        assert L.attn_fwd_dropout(ctypes.byref(small), fake, fake, fake, p, fake, need, fake, fake,
+                                  fake, 1 << 40, s) == -1
+        assert L.attn_bwd_dropout(ctypes.byref(small), fake, fake, fake, fake, fake, fake, p, fake,
+                                  need, fake, fake, fake, fake, 1 << 40, s) == -1
+    assert L.attn_dropout_mask(ctypes.byref(small), 0.1, u64(1), u64(0), null, need, s) == -1
+    assert L.attn_dropout_mask(ctypes.byref(small), 0.1, u64(1), u64(0), fake, need - 1, s) == -1
+    assert L.attn_fwd_dropout(ctypes.byref(small), fake, fake, fake, 0.1, fake, need - 1, fake,
+                              fake, fake, 1 << 40, s) == -1
+    assert L.attn_bwd_dropout(ctypes.byref(small), fake, fake, fake, fake, fake, fake, 0.1, null,
+                              need, fake, fake, fake, fake, 1 << 40, s) == -1
+    f32 = cfg(dtype=bd.ATTN_F32)
+    assert L.attn_fwd_dropout(ctypes.byref(f32), fake, fake, fake, 0.1, fake, 1 << 40, fake, fake,
+                              fake, 1 << 40, s) == -2
+    empty = cfg(T=0)
+    assert L.attn_dropout_mask_bytes(ctypes.byref(empty)) == 0
+    assert L.attn_dropout_mask(ctypes.byref(empty), 0.1, u64(1), u64(0), null, 0, s) == 0
+    assert L.attn_fwd_dropout(ctypes.byref(empty), null, null, null, 0.1, null, 0, null, null,
+                              null, 0, s) == 0
+
+
 def test_decode_config_validation(L):
     o = bd.AttnOptions(softcap=50.0, rope=True)
     assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, 2048, o))) == 0

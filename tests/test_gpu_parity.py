@@ -10,12 +10,13 @@ import sys
 import numpy as np
 import pytest
 
-from causal_attention_02_amd import AttnOptions, attn_bwd, attn_decode, attn_extend, attn_fwd
+from causal_attention_02_amd import (AttnOptions, attn_bwd, attn_decode, attn_dropout_mask,
+                                    attn_extend, attn_fwd)
 from causal_attention_02_amd.inputs import (WORKLOADS, Workload, make_decode_inputs,
                                             make_extend_inputs, make_segment_ids,
                                             make_train_inputs, round_to_bf16)
 from oracle import (attention_backward, attention_decode, attention_extend, attention_forward,
-                    rms_normalize, rope_rotate)
+                    dropout_fields, dropout_keep, dropout_threshold, rms_normalize, rope_rotate)
 from tests.util import (TOL_F32_MAXABS, TOL_GRAD, TOL_LSE_BF16, TOL_O, max_abs, rel_l2, to_dev,
                         to_host)
 
@@ -333,6 +334,146 @@ def test_packed_full_size_sampled():
         sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
               got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
         check_bf16(w, sl, ref_f, ref_b, f"{w.name}[b={b},g={g}]")
+
+
+# --------------------------------------------------------------------------------------------
+# Dropout on the attention weights
+# --------------------------------------------------------------------------------------------
+def mask_layouts(mask_t, B, H, T):
+    """The keep-mask buffer as its two word arrays (rows, cols), uint32 [B, H, T, pitch]."""
+    pitch = 2 * ((T + 63) // 64)
+    n = B * H * T * pitch
+    half = (n * 4 + 255) // 256 * 256 // 4
+    words = mask_t.cpu().numpy().view(np.uint32)
+    return words[:n].reshape(B, H, T, pitch), words[half:half + n].reshape(B, H, T, pitch)
+
+
+def oracle_mask_words(b, h, H, T, p, seed, offset):
+    """Keep words of head (b, h) from the oracle's Philox fields over 32-padded rows and columns:
+    rows[i, w] bit c keeps (i, 32 w + c); cols[j, w] bit c keeps (32 w + c, j)."""
+    t, _ = dropout_threshold(p)
+    nt = (T + 31) // 32
+    Tp = 32 * nt
+    keep = np.stack([dropout_fields(b, h, H, i, Tp, seed, offset) >= t for i in range(Tp)])
+    sh = np.arange(32, dtype=np.uint64)
+    pack = lambda m: (m.reshape(Tp, nt, 32).astype(np.uint64) << sh).sum(-1).astype(np.uint32)
+    return pack(keep), pack(keep.T.copy())
+
+
+def band_tiles(T, window):
+    """(query tile, key tile) pairs of 32 x 32 tiles that meet the causal / window band."""
+    nt = (T + 31) // 32
+    out = []
+    for qt in range(nt):
+        lo = max(0, qt * 32 - window + 1) // 32 if window > 0 else 0
+        out += [(qt, kt) for kt in range(lo, qt + 1)]
+    return out
+
+
+def check_mask_words(mask_t, B, H, T, window, p, seed, offset, heads):
+    rows, cols = mask_layouts(mask_t, B, H, T)
+    band = band_tiles(T, window)
+    for b, h in heads:
+        er, ec = oracle_mask_words(b, h, H, T, p, seed, offset)
+        for qt, kt in band:
+            i = np.arange(qt * 32, min(qt * 32 + 32, T))
+            j = np.arange(kt * 32, min(kt * 32 + 32, T))
+            np.testing.assert_array_equal(rows[b, h, i, kt], er[i, kt], err_msg=f"rows b{b} h{h}")
+            np.testing.assert_array_equal(cols[b, h, j, qt], ec[j, qt], err_msg=f"cols b{b} h{h}")
+
+
+MASK_CASES = [(2, 3, 77, 0, 0.1, 42, 0), (1, 2, 300, 100, 0.5, 2 ** 63 + 5, 7),
+              (1, 1, 32, 0, 0.0, 1, 0), (3, 2, 129, 1, 0.9, 12345, 2 ** 40)]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"T{c[2]}_W{c[3]}_p{c[4]}" for c in MASK_CASES])
+def test_dropout_mask_bits(case):
+    import torch
+    B, H, T, W, p, seed, off = case
+    _say(f"case dropout mask B={B} H={H} T={T} W={W} p={p} seed={seed} offset={off}")
+    q = torch.zeros((B, H, T, 64), dtype=torch.bfloat16, device="cuda")
+    m = attn_dropout_mask(q, q, p, seed, off, AttnOptions(window=W))
+    torch.cuda.synchronize()
+    check_mask_words(m, B, H, T, W, p, seed, off, [(b, h) for b in range(B) for h in range(H)])
+
+
+def gpu_fwd_bwd_dropout(w, q, k, v, dO, offset=0):
+    import torch
+    tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+    m = attn_dropout_mask(tq, tk, w.dropout, w.seed, offset, opts_of(w))
+    o, lse = attn_fwd(tq, tk, tv, opts_of(w), dropout_p=w.dropout, dropout_mask=m)
+    g = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w), dropout_p=w.dropout, dropout_mask=m)
+    torch.cuda.synchronize()
+    return (to_host(o), to_host(lse)) + tuple(to_host(x) for x in g), m
+
+
+DROPOUT_CASES = [
+    Workload("drop_gpt", B=2, T=256, Hq=12, Hkv=12, D=64, dropout=0.1),
+    Workload("drop_181m", B=2, T=300, Hq=8, Hkv=4, D=96, softcap=50.0, rope=True, qk_norm=True,
+             dropout=0.2),
+    Workload("drop_window", B=1, T=333, Hq=6, Hkv=3, D=128, window=100, rope=True, qk_norm=True,
+             dropout=0.5),
+    Workload("drop_d32_ragged", B=2, T=65, Hq=4, Hkv=2, D=32, softcap=5.0, dropout=0.1),
+    Workload("drop_cap_exp", B=1, T=200, Hq=2, Hkv=1, D=64, softcap=0.5, dropout=0.3),
+    Workload("drop_rate0", B=1, T=130, Hq=2, Hkv=1, D=64, rope=True, dropout=0.0),
+    Workload("drop_T1", B=3, T=1, Hq=2, Hkv=1, D=32, dropout=0.5),
+]
+
+
+@pytest.mark.parametrize("w", DROPOUT_CASES, ids=[w.name for w in DROPOUT_CASES])
+def test_dropout_fwd_bwd(w):
+    _say(f"case {w.name}: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} W={w.window} "
+         f"cap={w.softcap} rope={w.rope} norm={w.qk_norm} p={w.dropout}")
+    q, k, v, dO = make_train_inputs(w)
+    got, _ = gpu_fwd_bwd_dropout(w, q, k, v, dO, offset=3)
+    keep = dropout_keep(w.B, w.Hq, w.T, w.dropout, w.seed, 3)
+    kw = dict(oracle_kw(w), dropout_p=w.dropout, dropout_keep=keep)
+    check_bf16(w, got, attention_forward(q, k, v, **kw), attention_backward(q, k, v, dO, **kw),
+               w.name, tol_grad=TOL_GRAD if w.T > 2 else 5e-2)
+
+
+def test_dropout_full_size_sampled():
+    w = WORKLOADS["gpt_pretrain_train_dropout"]
+    _say(f"case {w.name} full size: B={w.B} T={w.T} Hq={w.Hq} D={w.D} p={w.dropout}")
+    q, k, v, dO = make_train_inputs(w)
+    got, m = gpu_fwd_bwd_dropout(w, q, k, v, dO)
+    G = w.Hq // w.Hkv
+    t, _ = dropout_threshold(w.dropout)
+    samples = [(0, 0), (w.B // 2, w.Hkv // 2), (w.B - 1, w.Hkv - 1)]
+    check_mask_words(m, w.B, w.Hq, w.T, w.window, w.dropout, w.seed, 0,
+                     [(b, g * G) for b, g in samples])
+    for b, g in samples:
+        hs = slice(g * G, (g + 1) * G)
+        keep = np.stack([[dropout_fields(b, h, w.Hq, i, w.T, w.seed, 0) >= t for i in range(w.T)]
+                         for h in range(g * G, (g + 1) * G)])[None]
+        qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
+        kw = dict(oracle_kw(w), dropout_p=w.dropout, dropout_keep=keep)
+        ref_f = attention_forward(qs, ks, vs, **kw)
+        ref_b = attention_backward(qs, ks, vs, dos, **kw)
+        sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
+              got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
+        check_bf16(w, sl, ref_f, ref_b, f"{w.name}[b={b},g={g}]")
+
+
+def test_dropout_mask_reuse_is_deterministic():
+    # The same mask gives the same result; another offset gives another mask.
+    import torch
+    w = DROPOUT_CASES[1]
+    q, k, v, dO = make_train_inputs(w)
+    a, m1 = gpu_fwd_bwd_dropout(w, q, k, v, dO, offset=0)
+    b, m2 = gpu_fwd_bwd_dropout(w, q, k, v, dO, offset=0)
+    c, m3 = gpu_fwd_bwd_dropout(w, q, k, v, dO, offset=1)
+
+    def band_words(m):  # only words of tiles in the band are written
+        rows, cols = mask_layouts(m, w.B, w.Hq, w.T)
+        return np.concatenate([np.concatenate([rows[:, :, qt * 32:qt * 32 + 32, kt].ravel(),
+                                               cols[:, :, kt * 32:kt * 32 + 32, qt].ravel()])
+                               for qt, kt in band_tiles(w.T, w.window)])
+    assert np.array_equal(band_words(m1), band_words(m2))
+    assert not np.array_equal(band_words(m1), band_words(m3))
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert rel_l2(c[0], a[0]) > 1e-2
 
 
 # --------------------------------------------------------------------------------------------

@@ -600,6 +600,10 @@ def test_workload_shapes_match_pages():
     w = WORKLOADS["gpt_pretrain_train"]
     assert (w.B, w.T, w.Hq, w.Hkv, w.D) == (gp["batch_size"], gp["context_length"], gp["num_heads"],
                                             gp["num_heads"], gp["d_model"] // gp["num_heads"])
+    w = WORKLOADS["gpt_pretrain_train_dropout"]
+    assert (w.B, w.T, w.Hq, w.Hkv, w.D, w.dropout) == (
+        gp["batch_size"], gp["context_length"], gp["num_heads"], gp["num_heads"],
+        gp["d_model"] // gp["num_heads"], gp["mha_dropout_rate"])
     w = WORKLOADS["gpt_pretrain_decode"]
     demo = gp["kv_cache_demo"]
     assert (w.B, w.T, w.len_lo, w.Hq, w.D) == (demo["batch"], demo["context_length"],
