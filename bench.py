@@ -65,6 +65,15 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+def visible_tiles32(T, window):
+    """32 x 32 (query, key) tiles that meet the causal / window band of one head."""
+    n = 0
+    for qt in range((T + 31) // 32):
+        lo = max(0, qt * 32 - window + 1) // 32 if window > 0 else 0
+        n += qt - lo + 1
+    return n
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -117,6 +126,7 @@ def main():
     # fwd + bwd
     # ------------------------------------------------------------------------------------
     def train_case(w, steps, warmup, trace=False, ids=None):
+        """Time fwd + bwd; with w.dropout > 0 each step also draws a fresh keep mask."""
         q, k, v, dO = make_train_inputs(w)
         tids = None if ids is None else torch.from_numpy(ids).to(dev)
         tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(dO)
@@ -136,11 +146,21 @@ def main():
             nb = bd.lib().attn_bwd_packed_workspace_bytes(ctypes.byref(cfg))
         wsf = torch.empty(max(int(nf), 1), dtype=torch.uint8, device=dev)
         wsb = torch.empty(max(int(nb), 1), dtype=torch.uint8, device=dev)
+        p = w.dropout
+        mask = None
+        if p > 0:
+            nm = bd.lib().attn_dropout_mask_bytes(ctypes.byref(cfg))
+            mask = torch.empty(max(int(nm), 1), dtype=torch.uint8, device=dev)
+        calls = [0]
 
         def step():
-            bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf, segment_ids=tids)
+            if mask is not None:
+                bd.attn_dropout_mask(tq, tk, p, w.seed, calls[0], opts, out=mask)
+                calls[0] += 1
+            bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf, segment_ids=tids,
+                        dropout_p=p, dropout_mask=mask)
             bd.attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb,
-                        segment_ids=tids)
+                        segment_ids=tids, dropout_p=p, dropout_mask=mask)
 
         for _ in range(warmup):
             step()
@@ -192,13 +212,22 @@ def main():
                         algorithmic_flops_per_launch=algo_per_pair[fam] * pairs)
         result["roofline"] = roof
         for name in ("flaxchat_full", "flaxchat_w512", "gpt_pretrain_train",
-                     "gpt2xl_instruct_train"):
+                     "gpt_pretrain_train_dropout", "gpt2xl_instruct_train"):
             w = WORKLOADS[name]
             log(f"[bench] fwd+bwd {name}")
-            ms2, per2, _ = train_case(w, max(args.steps // 2, 3), 2)
+            drop = w.dropout > 0
+            ms2, per2, k2 = train_case(w, max(args.steps // 2, 3), 2, trace=drop)
             tf2 = train_flops(w) / (ms2 * 1e-3) / 1e12
             extra[name] = dict(ms_per_step=ms2, ms_median=float(np.median(per2)), tflops=tf2,
                                pct_peak=100 * tf2 / PEAK_BF16_TFLOPS)
+            if drop:
+                # The mask kernel is integer-ALU work: report its rate in keep decisions per second
+                # over the 32 x 32 tiles it fills.
+                ktimes = {n: t / c for n, (c, t) in k2.items()}
+                tiles = visible_tiles32(w.T, w.window) * w.B * w.Hq
+                extra[name].update(
+                    dropout=w.dropout, kernels_ms={n: round(a, 4) for n, a in ktimes.items()},
+                    mask_gdecisions_per_s=tiles * 1024 / (ktimes["dropout_mask"] * 1e-3) / 1e9)
             log(f"[bench] {name}: {ms2:.3f} ms/step  {tf2:.1f} TFLOP/s")
         # SFT-style packed rows (segment ids) on the 181M shapes.
         wp = WORKLOADS["gqa181m_sft_packed"]

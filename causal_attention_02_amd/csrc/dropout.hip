@@ -25,13 +25,27 @@ struct DropArgs {
   uint64_t seed, offset;
 };
 
+// Full 64 x 64 -> 128-bit product m * x from four 32 x 32 -> 64 products (v_mad_u64_u32);
+// none of the partial sums can overflow 64 bits.
+template <uint64_t M>
+__device__ __forceinline__ void mulhilo64(uint64_t x, uint64_t& lo, uint64_t& hi) {
+  constexpr uint32_t ml = (uint32_t)M, mh = (uint32_t)(M >> 32);
+  const uint32_t xl = (uint32_t)x, xh = (uint32_t)(x >> 32);
+  const uint64_t p0 = (uint64_t)xl * ml;
+  const uint64_t p1 = (uint64_t)xl * mh + (uint32_t)(p0 >> 32);
+  const uint64_t p2 = (uint64_t)xh * ml + (uint32_t)p1;
+  hi = (uint64_t)xh * mh + (uint32_t)(p1 >> 32) + (uint32_t)(p2 >> 32);
+  lo = (p2 << 32) | (uint32_t)p0;
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t (&x)[4], uint64_t k0, uint64_t k1) {
   constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
   constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t lo0 = kM0 * x[0], hi0 = __umul64hi(kM0, x[0]);
-    const uint64_t lo1 = kM1 * x[2], hi1 = __umul64hi(kM1, x[2]);
+    uint64_t lo0, hi0, lo1, hi1;
+    mulhilo64<kM0>(x[0], lo0, hi0);
+    mulhilo64<kM1>(x[2], lo1, hi1);
     const uint64_t y0 = hi1 ^ x[1] ^ k0, y2 = hi0 ^ x[3] ^ k1;
     x[0] = y0;
     x[1] = lo1;
