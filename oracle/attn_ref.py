@@ -50,7 +50,12 @@ project's design notes):
   position L_b + i, its key is rotated at that position (and normalised) before it
   is stored, and rows that would land at or past Lmax are not stored (their queries
   return zero rows).
-
+* Left-padded batches (181M model card, inference notes: left-padded prompts with
+  right-aligned generation through a KV cache, attending only the compact active slice):
+  cache_start[b] = S_b rows of padding precede sequence b's first token, so row r holds
+  the token at position r - S_b; only rows S_b .. (the query's row) are attended, and a
+  query whose own row is below S_b (a padding token) returns a zero row.  Without
+  cache_start, S_b = 0.
 * Attention dropout ("GPT pretraining" page, section "Multihead Attention": dropout on the
   attention weights after the softmax, before they multiply V; rate 0.1 in the page's GPT
   configuration): inverted dropout, as the page's dropout layer does -- a weight is kept
@@ -364,12 +369,13 @@ def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=F
 
 
 def attention_decode(q, k_cache, v_cache, cache_len, *, softcap=0.0, scale=None, rope=False,
-                     rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
-    """One-token decode: q [B,Hq,d] attends over the first L_b rows of k/v_cache [B,Hkv,Lmax,d].
+                     rope_base=10000.0, qk_norm=False, norm_eps=1e-6, cache_start=None):
+    """One-token decode: q [B,Hq,d] attends over rows S_b .. L_b - 1 of k/v_cache [B,Hkv,Lmax,d].
 
     The cached keys are taken as already rotated (and normalised, when QK-norm is on); only
-    the query is rotated, at position L_b - 1, and normalised.  cache_len is clamped to
-    [0, Lmax]; a sequence with L_b = 0 gives a zero output row.  Returns o [B,Hq,d].
+    the query is rotated, at position L_b - 1 - S_b, and normalised.  cache_len is clamped to
+    [0, Lmax] and cache_start (S_b, default 0) to [0, L_b]; an empty range gives a zero
+    output row.  Returns o [B,Hq,d].
     """
     q = np.asarray(q, dtype=np.float64)
     kc = np.asarray(k_cache, dtype=np.float64)
@@ -386,19 +392,22 @@ def attention_decode(q, k_cache, v_cache, cache_len, *, softcap=0.0, scale=None,
     o = np.zeros((B, Hq, d))
     for b in range(B):
         L = int(min(max(int(cache_len[b]), 0), Lmax))
-        if L == 0:
+        S0 = 0 if cache_start is None else int(min(max(int(cache_start[b]), 0), L))
+        if L == S0:
             continue
-        qhat, _ = _prologue(q[b][:, None, :], np.array([L - 1]), rope, rope_base, qk_norm, norm_eps)
+        qhat, _ = _prologue(q[b][:, None, :], np.array([L - 1 - S0]), rope, rope_base, qk_norm,
+                            norm_eps)
         for h in range(Hq):
             g = h // group
-            _, s = _scores(qhat[h], kc[b, g, :L], scale, softcap)
+            _, s = _scores(qhat[h], kc[b, g, S0:L], scale, softcap)
             P, _ = _softmax_rows(s, np.ones_like(s, dtype=bool))
-            o[b, h] = (P @ vc[b, g, :L])[0]
+            o[b, h] = (P @ vc[b, g, S0:L])[0]
     return o
 
 
 def attention_extend(q, k_new, v_new, k_cache, v_cache, cache_len, *, window=0, softcap=0.0,
-                     scale=None, rope=False, rope_base=10000.0, qk_norm=False, norm_eps=1e-6):
+                     scale=None, rope=False, rope_base=10000.0, qk_norm=False, norm_eps=1e-6,
+                     cache_start=None):
     """S new tokens per sequence against a KV cache ("GPT pretraining" page, "Bonus: KV Caching").
 
     q [B,Hq,S,d], k_new/v_new [B,Hkv,S,d] are raw (before RoPE / QK-norm); the caches
@@ -408,6 +417,9 @@ def attention_extend(q, k_new, v_new, k_cache, v_cache, cache_len, *, window=0, 
     j > p - window with a window) -- the page's offset rule with offset = L_b.
     cache_len is clamped to [0, Lmax]; tokens with p >= Lmax are not stored and give zero
     output rows.  Returns (o [B,Hq,S,d], k_cache', v_cache'); the inputs are not modified.
+    With cache_start (S_b, clamped to [0, Lmax]) the rows below S_b are left padding: the
+    token in row r sits at position r - S_b (its key is rotated there), only rows >= S_b are
+    attended, and new tokens whose row is below S_b (padding) are stored but give zero rows.
     """
     q = np.asarray(q, dtype=np.float64)
     kn = np.asarray(k_new, dtype=np.float64)
@@ -431,21 +443,24 @@ def attention_extend(q, k_new, v_new, k_cache, v_cache, cache_len, *, window=0, 
     o = np.zeros((B, Hq, S, d))
     for b in range(B):
         L = int(min(max(int(cache_len[b]), 0), Lmax))
+        S0 = 0 if cache_start is None else int(min(max(int(cache_start[b]), 0), Lmax))
         n = min(S, Lmax - L)  # tokens that fit in the cache
         if n <= 0:
             continue
-        pos = L + np.arange(n)
+        rows = L + np.arange(n)
+        pos = rows - S0
         khat, _ = _prologue(kn[b][:, :n], pos, rope, rope_base, qk_norm, norm_eps)
         kc[b, :, L:L + n] = khat
         vc[b, :, L:L + n] = vn[b][:, :n]
         qhat, _ = _prologue(q[b][:, :n], pos, rope, rope_base, qk_norm, norm_eps)
         j = np.arange(L + n)[None, :]
-        allowed = j <= pos[:, None]
+        allowed = (j <= rows[:, None]) & (j >= S0)
         if window > 0:
-            allowed &= (pos[:, None] - j) < window
+            allowed &= (rows[:, None] - j) < window
+        real = rows >= S0  # padding tokens (rows below S_b) give zero rows
         for h in range(Hq):
             g = h // group
-            _, sc = _scores(qhat[h], kc[b, g, :L + n], scale, softcap)
-            P, _ = _softmax_rows(sc, allowed)
-            o[b, h, :n] = P @ vc[b, g, :L + n]
+            _, sc = _scores(qhat[h][real], kc[b, g, :L + n], scale, softcap)
+            P, _ = _softmax_rows(sc, allowed[real])
+            o[b, h, :n][real] = P @ vc[b, g, :L + n]
     return o, kc, vc

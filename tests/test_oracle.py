@@ -454,7 +454,7 @@ def test_single_run_is_plain_attention():
 # Extend: S new tokens against a KV cache (append, then attend with the offset mask).
 # ------------------------------------------------------------------------------------
 def brute_force_extend(q, kn, vn, kc, vc, lens, window, softcap, rope, qk_norm, base=10000.0,
-                       eps=1e-6):
+                       eps=1e-6, starts=None):
     B, Hq, S, d = q.shape
     Hkv, Lmax = kc.shape[1], kc.shape[2]
     scale = 1.0 / math.sqrt(d)
@@ -462,17 +462,18 @@ def brute_force_extend(q, kn, vn, kc, vc, lens, window, softcap, rope, qk_norm, 
     K, V = kc.copy(), vc.copy()
     for b in range(B):
         L = min(max(int(lens[b]), 0), Lmax)
+        s0 = 0 if starts is None else min(max(int(starts[b]), 0), Lmax)  # left padding rows
         for g, i in itertools.product(range(Hkv), range(S)):
             if L + i < Lmax:
-                K[b, g, L + i] = _bf_prologue(kn[b, g, i], L + i, rope, base, qk_norm, eps)
+                K[b, g, L + i] = _bf_prologue(kn[b, g, i], L + i - s0, rope, base, qk_norm, eps)
                 V[b, g, L + i] = vn[b, g, i]
         for h, i in itertools.product(range(Hq), range(S)):
             p = L + i
-            if p >= Lmax:
+            if p >= Lmax or p < s0:
                 continue
             g = h * Hkv // Hq
-            qi = _bf_prologue(q[b, h, i], p, rope, base, qk_norm, eps)
-            keys = [j for j in range(p + 1) if window == 0 or p - j < window]
+            qi = _bf_prologue(q[b, h, i], p - s0, rope, base, qk_norm, eps)
+            keys = [j for j in range(s0, p + 1) if window == 0 or p - j < window]
             sc = []
             for j in keys:
                 s_ = scale * sum(a * c for a, c in zip(qi, K[b, g, j]))
@@ -781,3 +782,67 @@ def test_dropout_is_unbiased():
                      for s in range(n)])
     se = outs.std(axis=0) / math.sqrt(n)
     assert np.all(np.abs(outs.mean(axis=0) - plain) <= 5 * se + 1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# Left-padded batches (181M model card, inference notes): rows below cache_start[b] are padding.
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_leftpad_extend_matches_brute_force(flags):
+    rng = np.random.default_rng(50)
+    B, Hq, Hkv, S, d, Lmax = 4, 2, 1, 6, 4, 12
+    q, kn, vn = rnd(rng, B, Hq, S, d), rnd(rng, B, Hkv, S, d), rnd(rng, B, Hkv, S, d)
+    kc, vc = rnd(rng, B, Hkv, Lmax, d), rnd(rng, B, Hkv, Lmax, d)
+    lens, starts = np.array([0, 3, 5, 9]), np.array([2, 1, 5, 11])
+    got = attention_extend(q, kn, vn, kc, vc, lens, cache_start=starts, **flags)
+    want = brute_force_extend(q, kn, vn, kc, vc, lens, starts=starts, **flags)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS[:3])
+def test_leftpad_decode_equals_compact_slice(flags):
+    # Padding rows (filled with large garbage) change nothing; the query sits at position
+    # L - 1 - S of the compact sequence.
+    flags = {k: v for k, v in flags.items() if k != "window"}
+    rng = np.random.default_rng(51)
+    B, Hq, Hkv, d, Lmax = 4, 4, 2, 8, 20
+    q = rnd(rng, B, Hq, d)
+    compact = rnd(rng, B, Hkv, Lmax, d), rnd(rng, B, Hkv, Lmax, d)
+    lens = np.array([5, 1, 20, 7])
+    starts = np.array([3, 0, 0, 13])
+    kc, vc = 1e3 * rnd(rng, B, Hkv, Lmax, d), 1e3 * rnd(rng, B, Hkv, Lmax, d)
+    for b in range(B):
+        n = min(lens[b], Lmax - starts[b])
+        kc[b, :, starts[b]:starts[b] + n] = compact[0][b, :, :n]
+        vc[b, :, starts[b]:starts[b] + n] = compact[1][b, :, :n]
+    got = attention_decode(q, kc, vc, np.minimum(starts + lens, Lmax), cache_start=starts, **flags)
+    want = attention_decode(q, compact[0], compact[1], np.minimum(lens, Lmax - starts), **flags)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+    # start at or past the length: an empty slice, a zero row
+    z = attention_decode(q, kc, vc, np.array([3, 0, 4, 2]), cache_start=np.array([3, 0, 9, 2]),
+                         **flags)
+    assert not z.any()
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_leftpad_prefill_equals_forward_of_each_prompt(flags):
+    # A left-padded batch prefilled in one extend step: each prompt's rows equal the causal
+    # forward of that prompt alone, padding rows are zero, and the stored keys are the
+    # prompt's own (rotated from position 0).
+    rng = np.random.default_rng(52)
+    B, Hq, Hkv, S, d = 3, 2, 1, 9, 4
+    pads = np.array([0, 4, 8])
+    q, kn, vn = rnd(rng, B, Hq, S, d), rnd(rng, B, Hkv, S, d), rnd(rng, B, Hkv, S, d)
+    kc, vc = np.zeros((B, Hkv, S, d)), np.zeros((B, Hkv, S, d))
+    o, K, V = attention_extend(q, kn, vn, kc, vc, np.zeros(B, dtype=int), cache_start=pads,
+                               **flags)
+    for b in range(B):
+        P = pads[b]
+        ref, _ = attention_forward(q[b:b + 1, :, P:], kn[b:b + 1, :, P:], vn[b:b + 1, :, P:],
+                                   **flags)
+        np.testing.assert_allclose(o[b, :, P:], ref[0], atol=1e-12)
+        assert not o[b, :, :P].any()
+        _, Kc, _ = attention_extend(q[b:b + 1, :, P:], kn[b:b + 1, :, P:], vn[b:b + 1, :, P:],
+                                    kc[b:b + 1, :, :S - P], vc[b:b + 1, :, :S - P], [0], **flags)
+        np.testing.assert_allclose(K[b, :, P:], Kc[0], atol=1e-12)
