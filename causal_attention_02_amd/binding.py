@@ -23,7 +23,7 @@ EXPORTED = [
     "attn_check_cfg", "attn_check_decode_cfg", "attn_check_extend_cfg", "attn_fwd", "attn_bwd",
     "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
     "attn_trace_enable", "attn_trace_read", "attn_dropout_mask_bytes", "attn_dropout_mask",
-    "attn_fwd_dropout", "attn_bwd_dropout",
+    "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_leftpad", "attn_extend_leftpad",
 ]
 
 
@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.restype = ctypes.c_int
         L.attn_extend.argtypes = [ecfgp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_extend.restype = ctypes.c_int
+        L.attn_decode_leftpad.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_decode_leftpad.restype = ctypes.c_int
+        L.attn_extend_leftpad.argtypes = [ecfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_extend_leftpad.restype = ctypes.c_int
         L.attn_status_str.argtypes = [ctypes.c_int]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_trace_enable.argtypes = [ctypes.c_int]
@@ -350,8 +354,10 @@ def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, d
 
 
 def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None, *, split_len=0,
-                out=None, workspace=None, stream=None):
-    """Decode (bf16): q [B,Hq,D], caches [B,Hkv,Lmax,D], cache_len int32 [B] -> o [B,Hq,D]."""
+                out=None, workspace=None, stream=None, cache_start=None):
+    """Decode (bf16): q [B,Hq,D], caches [B,Hkv,Lmax,D], cache_len int32 [B] -> o [B,Hq,D].
+
+    cache_start (int32 [B], optional): left-padded batches, rows below it are padding."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, D = q.shape
@@ -366,6 +372,13 @@ def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None,
     cfg = make_decode_cfg(B, Hq, Hkv, D, Lmax, opts, split_len)
     _check(lib().attn_check_decode_cfg(ctypes.byref(cfg)), "attn_decode")
     ws = _workspace(int(lib().attn_decode_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+    if cache_start is not None:
+        _need(cache_start, (B,), torch.int32, "cache_start")
+        st = lib().attn_decode_leftpad(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(cache_start), _ptr(cache_len), _ptr(o), _ptr(ws),
+                                       ctypes.c_size_t(_nbytes(ws)), _stream(stream))
+        _check(st, "attn_decode_leftpad")
+        return o
     st = lib().attn_decode(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len),
                            _ptr(o), _ptr(ws),
                            ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
@@ -375,10 +388,10 @@ def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None,
 
 
 def attn_extend(q, k_new, v_new, k_cache, v_cache, cache_len, opts: AttnOptions | None = None, *,
-                out=None, stream=None):
+                out=None, stream=None, cache_start=None):
     """S new tokens against a KV cache (bf16): q [B,Hq,S,D], k_new/v_new [B,Hkv,S,D], caches
     [B,Hkv,Lmax,D] (rows cache_len[b] .. cache_len[b]+S-1 are written), cache_len int32 [B]
-    (not modified) -> o [B,Hq,S,D]."""
+    (not modified) -> o [B,Hq,S,D].  cache_start (int32 [B], optional): left-padded batches."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, S, D = q.shape
@@ -393,6 +406,13 @@ def attn_extend(q, k_new, v_new, k_cache, v_cache, cache_len, opts: AttnOptions 
     o = torch.empty_like(q) if out is None else out
     _need(o, q.shape, bf, "out")
     cfg = make_extend_cfg(B, S, Hq, Hkv, D, Lmax, opts)
+    if cache_start is not None:
+        _need(cache_start, (B,), torch.int32, "cache_start")
+        st = lib().attn_extend_leftpad(ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       _ptr(k_cache), _ptr(v_cache), _ptr(cache_start),
+                                       _ptr(cache_len), _ptr(o), _stream(stream))
+        _check(st, "attn_extend_leftpad")
+        return o
     st = lib().attn_extend(ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                            _ptr(v_cache), _ptr(cache_len), _ptr(o), _stream(stream))
     _check(st, "attn_extend")

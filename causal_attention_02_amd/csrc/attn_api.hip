@@ -405,8 +405,11 @@ int attn_bwd_dropout(const attn_cfg* c, const void* q, const void* k, const void
   return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream, mask, scale);
 }
 
-int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* cache_len, void* o, void* ws, size_t ws_bytes, void* stream) {
+// Decode and extend bodies; `start` (left padding rows per sequence, device int32 [B]) may be
+// null.
+static int decode_impl(const attn_decode_cfg* c, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* start, const int32_t* cache_len,
+                       void* o, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dcfg(c);
   if (st != ATTN_OK) return st;
   if (c->B == 0) return ATTN_OK;
@@ -414,33 +417,61 @@ int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, co
   if (c->Lmax > 0 && (!k_cache || !v_cache)) return ATTN_EINVAL;
   const size_t need = dec_ws(c);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
-  DecodeParams p{q, k_cache, v_cache, cache_len, o, (float*)ws, c->B, c->Hq, c->Hkv, c->D,
-                 c->Lmax, decode_split_len(c), decode_nsplit(c), eff_scale(c->scale, c->D),
-                 c->softcap, c->rope, c->rope_base, c->qk_norm, c->norm_eps};
+  DecodeParams p{q, k_cache, v_cache, cache_len, start, o, (float*)ws, c->B, c->Hq, c->Hkv,
+                 c->D, c->Lmax, decode_split_len(c), decode_nsplit(c),
+                 eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
+                 c->norm_eps};
   return launch_status(launch_decode(p, (hipStream_t)stream));
 }
 
-int attn_extend(const attn_extend_cfg* c, const void* q, const void* k_new, const void* v_new,
-                void* k_cache, void* v_cache, const int32_t* cache_len, void* o, void* stream) {
+static int extend_impl(const attn_extend_cfg* c, const void* q, const void* k_new,
+                       const void* v_new, void* k_cache, void* v_cache, const int32_t* start,
+                       const int32_t* cache_len, void* o, void* stream) {
   int st = check_ecfg(c);
   if (st != ATTN_OK) return st;
   if (c->B == 0 || c->S == 0) return ATTN_OK;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !o) return ATTN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   // 1. Store the new tokens' keys (RoPE at their positions, QK-norm) and values.
-  hipError_t e = launch_append_kv(k_new, v_new, k_cache, v_cache, cache_len, c->B, c->Hkv, c->S,
-                                  c->Lmax, c->D, c->rope, c->rope_base, c->qk_norm, c->norm_eps,
-                                  s);
-  // 2. The forward kernel in cache mode: queries at positions cache_len[b] + i over the cache.
+  hipError_t e = launch_append_kv(k_new, v_new, k_cache, v_cache, cache_len, start, c->B, c->Hkv,
+                                  c->S, c->Lmax, c->D, c->rope, c->rope_base, c->qk_norm,
+                                  c->norm_eps, s);
+  // 2. The forward kernel in cache mode: queries at rows cache_len[b] + i over the cache.
   if (e == hipSuccess) {
     FwdParams p{q, k_cache, v_cache, o, nullptr, c->B, c->S, c->Hq, c->Hkv, c->D, c->window,
                 eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
                 c->norm_eps};
     p.cache_len = cache_len;
+    p.cache_start = start;
     p.Lmax = c->Lmax;
     e = launch_fwd_bf16(p, s);
   }
   return launch_status(e);
+}
+
+int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* cache_len, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(c, q, k_cache, v_cache, nullptr, cache_len, o, ws, ws_bytes, stream);
+}
+
+int attn_decode_leftpad(const attn_decode_cfg* c, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_start, const int32_t* cache_len,
+                        void* o, void* ws, size_t ws_bytes, void* stream) {
+  if (!cache_start && c && c->B > 0) return ATTN_EINVAL;
+  return decode_impl(c, q, k_cache, v_cache, cache_start, cache_len, o, ws, ws_bytes, stream);
+}
+
+int attn_extend(const attn_extend_cfg* c, const void* q, const void* k_new, const void* v_new,
+                void* k_cache, void* v_cache, const int32_t* cache_len, void* o, void* stream) {
+  return extend_impl(c, q, k_new, v_new, k_cache, v_cache, nullptr, cache_len, o, stream);
+}
+
+int attn_extend_leftpad(const attn_extend_cfg* c, const void* q, const void* k_new,
+                        const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* cache_start, const int32_t* cache_len, void* o,
+                        void* stream) {
+  if (!cache_start && c && c->B > 0 && c->S > 0) return ATTN_EINVAL;
+  return extend_impl(c, q, k_new, v_new, k_cache, v_cache, cache_start, cache_len, o, stream);
 }
 
 int attn_trace_enable(int on) {

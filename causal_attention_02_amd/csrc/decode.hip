@@ -3,6 +3,8 @@
 // attends over the entire cached history; with offset = k_len - q_len = L - 1 every cached
 // key is visible).  The nanoGPT-JAX 181M model card's inference notes ask that only the
 // compact active part of the cache be attended; rows at or past cache_len[b] are never read.
+// With left-padded batches (the same notes: left-padded prompts, right-aligned generation)
+// rows below cache_start[b] are padding and are not read either; positions count from there.
 //
 // The work is HBM-bound (about 2 flops per byte), so it runs on the vector ALUs with
 // coalesced 16-byte loads, not on MFMA:
@@ -27,13 +29,23 @@ struct DecArgs {
   const bf16* kc;
   const bf16* vc;
   const int32_t* cache_len;
+  const int32_t* cache_start;  // left padding rows per sequence (or null: none)
   bf16* o;
   float* part;
   int B, Hq, Hkv, Lmax, split_len, nsplit;
   ScoreCoef sc;    // score transform (mode chosen on the host)
   float scale;
-  RowPrologue rp;  // query RoPE (position L - 1) and RMSNorm
+  RowPrologue rp;  // query RoPE (position L - 1 - start) and RMSNorm
 };
+
+// Active rows [first, L) of sequence b: L = cache_len clamped to [0, Lmax], first = the
+// left padding clamped to [0, L].
+__device__ __forceinline__ int active_end(const DecArgs& a, int b) {
+  return min(max(a.cache_len[b], 0), a.Lmax);
+}
+__device__ __forceinline__ int active_first(const DecArgs& a, int b, int L) {
+  return a.cache_start ? min(max(a.cache_start[b], 0), L) : 0;
+}
 
 constexpr int kDecWaves = 8;  // waves per split workgroup
 // Largest factor a running maximum may grow by before the accumulators are rescaled (log2).
@@ -120,19 +132,21 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(DecArgs
   const int hs = y % nsub;
   const int bg = y / nsub;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int L = min(max(a.cache_len[b], 0), a.Lmax);
-  const int start = split * a.split_len;
+  const int L = active_end(a, b);
+  const int first = active_first(a, b, L);
+  const int c0 = split * a.split_len;  // this chunk's rows: [c0, c0 + split_len) & [first, L)
+  const int start = max(c0, first);
+  const int stop = min(L, c0 + a.split_len);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int h0 = g * G + hs * HPB;
-  if (start >= L) {
-    // No active row in this chunk.  With a single chunk per sequence (L = 0) the output
-    // row is written here: zeros.
+  if (start >= stop) {
+    // No active row in this chunk.  With a single chunk per sequence (an empty active
+    // range) the output row is written here: zeros.
     if (a.nsplit == 1)
       for (int t = tid; t < HPB * D; t += 64 * NW)
         a.o[((int64_t)b * a.Hq + h0 + t / D) * D + t % D] = to_bf16(0.f);
     return;
   }
-  const int stop = min(L, start + a.split_len);
   const int npass = (stop - start + kPass - 1) / kPass;
 
   const int s4 = lane & 3;   // this lane's quarter of a row
@@ -162,15 +176,15 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(DecArgs
   Buf b0, b1;
   load(b0, 0);
 
-  // Query prologue while the first loads are in flight: wave hh rotates (position L - 1)
-  // and normalises head h0 + hh.
+  // Query prologue while the first loads are in flight: wave hh rotates (position
+  // L - 1 - first) and normalises head h0 + hh.
   if (w < HPB) {
     const int half = D / 2;
     const bool act = lane < half;
     const bf16* qr = a.q + ((int64_t)b * a.Hq + h0 + w) * D;
     float x1 = act ? from_bf16(qr[lane]) : 0.f;
     float x2 = act ? from_bf16(qr[lane + half]) : 0.f;
-    if (a.rp.rope && act) rope_pair(x1, x2, L - 1, a.rp.omega_rev[lane], false);
+    if (a.rp.rope && act) rope_pair(x1, x2, L - 1 - first, a.rp.omega_rev[lane], false);
     if (a.rp.qk_norm) {
       const float inv = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + a.rp.eps);
       x1 *= inv;
@@ -312,17 +326,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   if (wid >= a.B * a.Hq) return;
   const int lane = threadIdx.x & 63;
   const int b = wid / a.Hq;
-  const int L = min(max(a.cache_len[b], 0), a.Lmax);
+  const int L = active_end(a, b);
+  const int first = active_first(a, b, L);
+  // Chunks s0 .. n - 1 hold active rows (none when first == L); only they wrote partials.
   const int n = (L + a.split_len - 1) / a.split_len;
-  const float* pp = a.part + (int64_t)wid * a.nsplit * (D + 2);
+  const int s_first = first < L ? first / a.split_len : n;
+  const float* pp = a.part + ((int64_t)wid * a.nsplit + s_first) * (D + 2);
+  const int nact = n - s_first;
   const bool act = 2 * lane < D;
   float M = kNegBig;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, pp[s * (D + 2)]);
+  for (int s = lane; s < nact; s += 64) M = fmaxf(M, pp[s * (D + 2)]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   float lt = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int cnt = min(64, n - s0);
+  for (int s0 = 0; s0 < nact; s0 += 64) {
+    const int cnt = min(64, nact - s0);
     const float* ps = pp + (s0 + lane) * (D + 2);
     const float f = lane < cnt ? exp2_fast(ps[0] - M) : 0.f;
     if (lane < cnt) lt = fmaf(ps[1], f, lt);
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
     }
   }
   lt = wave_sum(lt);
-  const float inv = n > 0 ? 1.f / lt : 0.f;
+  const float inv = nact > 0 ? 1.f / lt : 0.f;
   if (act) {
     bf16x2 r;
     r[0] = to_bf16(o0 * inv);
@@ -389,6 +407,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.kc = (const bf16*)p.kc;
   a.vc = (const bf16*)p.vc;
   a.cache_len = p.cache_len;
+  a.cache_start = p.cache_start;
   a.o = (bf16*)p.o;
   a.part = p.part;
   a.B = p.B;

@@ -351,16 +351,22 @@ struct TileDma {
   }
   // The same copy with the offsets recomputed in place (three VALU ops per chunk) instead of
   // held in registers; the empty asm keeps the compiler from hoisting them out of the loop.
+  // LO: rows below `lo` (left padding of a cache) read row lo instead, so that whatever
+  // those rows hold (they are masked, but a NaN times a zero weight would still be NaN)
+  // never enters the tile.
+  template <bool LO = false>
   static __device__ __forceinline__ void copy_fresh(bf16* lds, const bf16* src, int r0, int T,
-                                                    int w, int l) {
+                                                    int w, int l, int lo = 0) {
     asm volatile("" : "+v"(l));
-    const int first = r0 * (D / 8), last = T * (D / 8) - 1;
+    const int first = r0 * (D / 8), last = T * (D / 8) - 1, lo_g = lo * (D / 8);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = w + NW * i;
       if (c < G) {
         const int pg = 64 * c + l;
-        const bf16* from = src + 8 * (int64_t)min(first + pg - pg / G, last);
+        int gsrc = min(first + pg - pg / G, last);
+        if constexpr (LO) gsrc = max(gsrc, lo_g);
+        const bf16* from = src + 8 * (int64_t)gsrc;
         __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
       }
     }

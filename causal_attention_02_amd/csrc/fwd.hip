@@ -34,6 +34,7 @@ struct FwdArgs {
   bf16* o;
   float* lse;                // may be null (extend: no LSE output)
   const int32_t* cache_len;  // extend: rows already cached per sequence (null in training)
+  const int32_t* cache_start;  // extend, left-padded batches: padding rows per sequence (or null)
   const int32_t* seg_start;  // packed rows: first index of each token's run, [B, T] (or null)
   const uint32_t* drop_rows; // dropout: row-layout keep mask [B, Hq, T, drop_pitch] (or null)
   int drop_pitch;
@@ -124,9 +125,14 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
   const int qrow = min(qi, nq - 1);
   const int window = a.window;
   const unsigned wlim = window > 0 ? (unsigned)window : 0x7fffffffu;
-  // Packed rows: this lane's query sees keys back to the start of its run only.
-  const int32_t* sst = PACKED ? a.seg_start + (int64_t)b * T : nullptr;
-  const unsigned lim = PACKED ? min(wlim, (unsigned)(qrow - sst[qrow] + 1)) : wlim;
+  // Packed rows: this lane's query sees keys back to the start of its run only.  A left-padded
+  // cache (extend) takes the same path with one run per sequence, from row cache_start[b]:
+  // positions count from there, and queries in padding rows get zero rows.
+  const int S0 = PACKED && a.cache_start ? min(max(a.cache_start[b], 0), Tk) : 0;
+  const int32_t* sst = PACKED && !a.cache_start ? a.seg_start + (int64_t)b * T : nullptr;
+  auto run_start = [&](int x) { return sst ? sst[x] : S0; };
+  const unsigned lim =
+      PACKED ? min(wlim, (unsigned)max(off + qrow - run_start(qrow) + 1, 0)) : wlim;
 
   const bf16* kbase = a.k + (int64_t)(b * a.Hkv + g) * Tk * D;
   const bf16* vbase = a.v + (int64_t)(b * a.Hkv + g) * Tk * D;
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int p = 0; p < 8; ++p) x[s][p] = (float)bq[s][p];
-      prologue_oplayout<NS>(x, off + qrow, gl, a.rp, D);
+      prologue_oplayout<NS>(x, off + qrow - S0, gl, a.rp, D);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -152,14 +158,15 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
   }
 
   const int k_end = min(nk, off + q0 + kBM);
-  const int k_begin = max(window > 0 ? max(0, off + q0 - window + 1) : 0, PACKED ? sst[q0] : 0);
+  const int k_begin =
+      max(window > 0 ? max(0, off + q0 - window + 1) : 0, PACKED ? run_start(q0) : 0);
   const int kt0 = k_begin / kBN, kt1 = (k_end - 1) / kBN;
 
   // Tile loads: rows past T read clamped, finite data whose scores the causal mask removes
   // (such keys lie after every query).
   auto dma = [&](int kt, int buf) {
-    TileDma<D, 4>::copy_fresh(buf ? sK1 : sK0, kbase, kt * kBN, nk, w, l);
-    TileDma<D, 4>::copy_fresh(buf ? sV1 : sV0, vbase, kt * kBN, nk, w, l);
+    TileDma<D, 4>::template copy_fresh<PACKED>(buf ? sK1 : sK0, kbase, kt * kBN, nk, w, l, S0);
+    TileDma<D, 4>::template copy_fresh<PACKED>(buf ? sV1 : sV0, vbase, kt * kBN, nk, w, l, S0);
     if constexpr (DROP) {
       // Wave w: keep word of block (w & 1) for queries q0 + 64 (w >> 1) + lane.
       const int row = min(q0 + 64 * (w >> 1) + l, T - 1);
@@ -181,8 +188,8 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
   const int pw0 = off + qw0, pw_last = off + min(qw0 + 31, nq - 1);
   // Earliest and latest run start among the wave's queries (packed rows; run starts grow
   // with the token index).
-  const int s_lo = PACKED ? sst[min(qw0, nq - 1)] : 0;
-  const int s_hi = PACKED ? sst[min(qw0 + 31, nq - 1)] : 0;
+  const int s_lo = PACKED ? run_start(min(qw0, nq - 1)) : 0;
+  const int s_hi = PACKED ? run_start(min(qw0 + 31, nq - 1)) : 0;
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
   }
 
   const float l_tot = pair_sum(l_run);
-  if (qi < nq) {
+  if (qi < nq && off + qi >= S0) {
     const float inv = (DROP ? a.drop_scale : 1.f) / l_tot;
     bf16* op = a.o + ((int64_t)bh * T + qi) * D;
 #pragma unroll
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
 // Launch the plain, packed-rows or dropout instantiation.
 template <int D, int MODE, bool FIXED>
 void launch_k(dim3 grid, hipStream_t s, const FwdArgs& a) {
-  if (a.seg_start)
+  if (a.seg_start || a.cache_start)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, FIXED, kVarPacked>), grid, dim3(256), 0, s, a);
   else if (a.drop_rows)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, FIXED, kVarDrop>), grid, dim3(256), 0, s, a);
@@ -468,6 +475,7 @@ hipError_t launch_fwd_bf16_d(const FwdParams& p, hipStream_t s) {
   a.o = (bf16*)p.o;
   a.lse = p.lse;
   a.cache_len = p.cache_len;
+  a.cache_start = p.cache_start;
   a.seg_start = p.seg_start;
   a.drop_rows = p.drop_rows;
   a.drop_pitch = dropout_pitch(p.T);

@@ -86,11 +86,13 @@ inline RowPrologue make_row_prologue(int rope, float rope_base, int qk_norm, flo
 // segment ids [B, T] -> first / last token index of every token's run (packed rows).
 hipError_t launch_segment_bounds(const int32_t* ids, int32_t* start, int32_t* end, int B, int T,
                                  hipStream_t s);
-// k_new/v_new [B, Hkv, S, D] -> cache rows cache_len[b] + i (RoPE at that position, QK-norm);
-// rows at or past Lmax are not written.
+// k_new/v_new [B, Hkv, S, D] -> cache rows cache_len[b] + i (RoPE at that row minus
+// cache_start[b], or at the row itself when cache_start is null; QK-norm); rows at or past
+// Lmax are not written.
 hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
-                            const int32_t* cache_len, int B, int Hkv, int S, int Lmax, int D,
-                            int rope, float rope_base, int qk_norm, float eps, hipStream_t s);
+                            const int32_t* cache_len, const int32_t* cache_start, int B, int Hkv,
+                            int S, int Lmax, int D, int rope, float rope_base, int qk_norm,
+                            float eps, hipStream_t s);
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s);
 
@@ -121,6 +123,9 @@ struct FwdParams {
   // (already holding the new keys), query i sits at position cache_len[b] + i.
   const int32_t* cache_len = nullptr;
   int Lmax = 0;
+  // Left-padded batches (extend only): rows below cache_start[b] are padding, positions count
+  // from there, and new tokens in padding rows get zero output rows (null: no padding).
+  const int32_t* cache_start = nullptr;
   // Packed rows: first token index of every token's run, [B, T] (null: one run per row).
   const int32_t* seg_start = nullptr;
   // Dropout on the weights: row-layout keep mask (null: none) and the kept-weight scale.
@@ -176,6 +181,7 @@ struct DecodeParams {
   const void* kc;       // [B, Hkv, Lmax, D]
   const void* vc;
   const int32_t* cache_len;
+  const int32_t* cache_start;  // left padding rows per sequence (null: none)
   void* o;              // [B, Hq, D]
   float* part;          // [B, Hq, nsplit, D + 2]
   int B, Hq, Hkv, D, Lmax, split_len, nsplit;

@@ -114,13 +114,15 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(const bf16* __restri
 
 // Append S new tokens to a KV cache ("GPT pretraining" page, "Bonus: KV Caching": compute
 // the new keys and values, append them, then attend).  Token i of sequence b lands in cache
-// row p = cache_len[b] + i (cache_len clamped to [0, Lmax]); its key is rotated at p and
-// normalised first, its value copied.  Rows with p >= Lmax are not written.  Same lane layout
+// row p = cache_len[b] + i (cache_len clamped to [0, Lmax]); its key is rotated at position
+// p - cache_start[b] (left padding rows; 0 without) and normalised first, its value copied.
+// Rows with p >= Lmax are not written.  Same lane layout
 // as prologue_bf16_kernel: 8 lanes per row, each owning 8 RoPE pairs.
 __global__ __launch_bounds__(256) void append_kv_kernel(const bf16* __restrict__ kn,
                                                         const bf16* __restrict__ vn,
                                                         bf16* __restrict__ kc, bf16* __restrict__ vc,
                                                         const int32_t* __restrict__ cache_len,
+                                                        const int32_t* __restrict__ cache_start,
                                                         int64_t rows, int S, int Hkv, int Lmax, int D,
                                                         RowPrologue rp) {
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);  // (b, g, i) row-major
@@ -130,7 +132,8 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const bf16* __restrict__
   const int i = in_range ? (int)(row - bg * S) : 0;
   const int b = (int)(bg / Hkv);
   const int L = in_range ? min(max(cache_len[b], 0), Lmax) : 0;
-  const int pos = L + i;
+  const int pos = L + i;  // cache row; the RoPE position counts from the first real row
+  const int first = (in_range && cache_start) ? min(max(cache_start[b], 0), Lmax) : 0;
   const bool act = in_range && pos < Lmax && u < D / 16;
   const int half = D / 2;
   float x1[8], x2[8];
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const bf16* __restrict__
   }
   if (rp.rope && act) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) rope_pair(x1[p], x2[p], pos, rp.omega_rev[8 * u + p], false);
+    for (int p = 0; p < 8; ++p)
+      rope_pair(x1[p], x2[p], pos - first, rp.omega_rev[8 * u + p], false);
   }
   if (rp.qk_norm) {
     float ss = 0.f;
@@ -182,14 +186,15 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const bf16* __restrict__
 }
 
 hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
-                            const int32_t* cache_len, int B, int Hkv, int S, int Lmax, int D,
-                            int rope, float rope_base, int qk_norm, float eps, hipStream_t s) {
+                            const int32_t* cache_len, const int32_t* cache_start, int B, int Hkv,
+                            int S, int Lmax, int D, int rope, float rope_base, int qk_norm,
+                            float eps, hipStream_t s) {
   const int64_t rows = (int64_t)B * Hkv * S;
   if (rows <= 0) return hipSuccess;
   TraceScope t("append_kv", s);
   hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s,
-                     (const bf16*)kn, (const bf16*)vn, (bf16*)kc, (bf16*)vc, cache_len, rows, S,
-                     Hkv, Lmax, D, make_row_prologue(rope, rope_base, qk_norm, eps, D));
+                     (const bf16*)kn, (const bf16*)vn, (bf16*)kc, (bf16*)vc, cache_len, cache_start,
+                     rows, S, Hkv, Lmax, D, make_row_prologue(rope, rope_base, qk_norm, eps, D));
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ class Workload:
     seg_hi: int = 0
     new_tokens: int = 0          # extend: tokens appended per sequence (cache lengths ~
                                  # U{len_lo .. T - new_tokens}, T = allocated rows)
+    leftpad: bool = False        # decode: left-padded batch, right-aligned in T cache rows
     dropout: float = 0.0         # dropout rate on the attention weights (0 = none); the keep
                                  # mask is drawn with generator seed `seed`, offset 0
     seed: int = SEED_BASE
@@ -86,6 +87,11 @@ WORKLOADS = {
     "gqa181m_decode": Workload("gqa181m_decode", B=64, T=2048, Hq=8, Hkv=4, D=96, softcap=50.0,
                                rope=True, backward=False, decode=True, len_lo=256,
                                seed=SEED_BASE + 4),
+    # Batched generation from left-padded prompts (181M model card, inference notes): every
+    # cache is right-aligned at 2048 rows and holds U{256..2048} real rows after its padding.
+    "gqa181m_decode_leftpad": Workload("gqa181m_decode_leftpad", B=64, T=2048, Hq=8, Hkv=4, D=96,
+                                       softcap=50.0, rope=True, backward=False, decode=True,
+                                       len_lo=256, leftpad=True, seed=SEED_BASE + 11),
     # SFT-style packed rows on the 181M shapes: each row holds sequences of U{64..1024} tokens.
     "gqa181m_sft_packed": Workload("gqa181m_sft_packed", B=16, T=2048, Hq=8, Hkv=4, D=96,
                                    softcap=50.0, rope=True, qk_norm=True, seg_lo=64, seg_hi=1024,
@@ -166,6 +172,15 @@ def packed_flops(w: Workload, ids) -> float:
         for n in np.diff(np.concatenate([[0], cuts, [len(row)]])):
             pairs += int(n) * (int(n) + 1) // 2
     return 14.0 * w.D * w.Hq * pairs
+
+
+def make_leftpad_decode_inputs(w: Workload, seed: int | None = None):
+    """make_decode_inputs for a left-padded batch: (q, k_cache, v_cache, cache_start,
+    cache_len) with cache_len = Lmax = w.T for every sequence and cache_start = T - (real rows),
+    real rows ~ U{len_lo .. T}."""
+    q, kc, vc, real = make_decode_inputs(w, seed)
+    lens = np.full(w.B, w.T, dtype=np.int32)
+    return q, kc, vc, (lens - real).astype(np.int32), lens
 
 
 def make_extend_inputs(w: Workload, seed: int | None = None):

@@ -232,6 +232,29 @@ int attn_decode(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
 int attn_extend(const attn_extend_cfg* cfg, const void* q, const void* k_new, const void* v_new,
                 void* k_cache, void* v_cache, const int32_t* cache_len, void* o, void* stream);
 
+/*
+ * attn_decode_leftpad, attn_extend_leftpad -- attn_decode / attn_extend for left-padded
+ * batches (the nanoGPT-JAX 181M model card's inference notes: left-padded prompts with
+ * right-aligned generation through a KV cache, attending only the compact active slice).
+ *   cache_start [B] device, int32 -- rows 0 .. cache_start[b] - 1 of sequence b's cache are
+ *             padding: they are never read, and the token in row r sits at position
+ *             r - cache_start[b] (keys stored by attn_extend_leftpad are rotated there; the
+ *             decode query sits at position cache_len[b] - 1 - cache_start[b]).  Clamped in
+ *             the kernels to [0, cache_len[b]] (decode) or [0, Lmax] (extend).
+ * Decode attends rows cache_start[b] .. cache_len[b] - 1 (an empty range gives a zero row).
+ * Extend attends rows cache_start[b] .. p for the token in row p; tokens whose row is below
+ * cache_start[b] (padding, e.g. the pad tokens of a left-padded prompt prefilled with
+ * cache_len = 0) are stored but their output rows are zero.  Every other argument and rule is
+ * that of attn_decode / attn_extend; cache_start may be NULL only when there is nothing to do.
+ */
+int attn_decode_leftpad(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_start, const int32_t* cache_len,
+                        void* o, void* ws, size_t ws_bytes, void* stream);
+int attn_extend_leftpad(const attn_extend_cfg* cfg, const void* q, const void* k_new,
+                        const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* cache_start, const int32_t* cache_len, void* o,
+                        void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(int status);
 

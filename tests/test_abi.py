@@ -146,6 +146,33 @@ def test_dropout_mask_bytes_and_validation(L):
                               null, 0, s) == 0
 
 
+def test_leftpad_entry_points_validation(L):
+    fake, null, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0), ctypes.c_void_p(0)
+    d = bd.make_decode_cfg(4, 8, 4, 96, 256, bd.AttnOptions(softcap=50.0, rope=True))
+    need = L.attn_decode_workspace_bytes(ctypes.byref(d))
+    # cache_start is required when there is work; the rest is checked as for attn_decode
+    assert L.attn_decode_leftpad(ctypes.byref(d), fake, fake, fake, null, fake, fake, fake, need,
+                                 s) == -1
+    assert L.attn_decode_leftpad(ctypes.byref(d), fake, fake, fake, fake, null, fake, fake, need,
+                                 s) == -1
+    assert L.attn_decode_leftpad(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake,
+                                 need - 1, s) == -3
+    e = bd.make_extend_cfg(4, 16, 8, 4, 96, 256, bd.AttnOptions(rope=True))
+    assert L.attn_extend_leftpad(ctypes.byref(e), fake, fake, fake, fake, fake, null, fake, fake,
+                                 s) == -1
+    assert L.attn_extend_leftpad(ctypes.byref(e), fake, fake, fake, fake, fake, fake, null, fake,
+                                 s) == -1
+    bad = bd.make_extend_cfg(4, 16, 8, 3, 96, 256, bd.AttnOptions())
+    assert L.attn_extend_leftpad(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake,
+                                 fake, s) == -1
+    nothing = bd.make_decode_cfg(0, 8, 4, 96, 256, bd.AttnOptions())
+    assert L.attn_decode_leftpad(ctypes.byref(nothing), null, null, null, null, null, null, null,
+                                 0, s) == 0
+    e0 = bd.make_extend_cfg(4, 0, 8, 4, 96, 256, bd.AttnOptions())
+    assert L.attn_extend_leftpad(ctypes.byref(e0), null, null, null, null, null, null, null, null,
+                                 s) == 0
+
+
 def test_decode_config_validation(L):
     o = bd.AttnOptions(softcap=50.0, rope=True)
     assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, 2048, o))) == 0
