@@ -105,7 +105,8 @@ def main():
     from causal_attention_02_amd.inputs import (WORKLOADS, decode_bytes, make_decode_inputs,
                                                 extend_flops, make_extend_inputs,
                                                 make_segment_ids, packed_flops,
-                                                make_train_inputs, train_flops, visible_pairs)
+                                                make_train_inputs, train_flops, visible_pairs,
+                                                make_leftpad_decode_inputs)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -322,6 +323,42 @@ def main():
         extra["gpt_pretrain_decode"] = dict(us_per_call=us_s,
                                             GBps=decode_bytes(ws, lens_s) / (us_s * 1e-6) / 1e9)
         log(f"[bench] gpt_pretrain_decode: {us_s:.1f} us/call")
+        # Left-padded batch (right-aligned caches of 2048 rows, U{256..2048} real rows each),
+        # over the same number of cache copies as the plain decode.
+        wl = WORKLOADS["gqa181m_decode_leftpad"]
+        ql, kcl, vcl, starts_l, lens_l = make_leftpad_decode_inputs(wl)
+        tql = to_dev(ql)
+        tkl0, tvl0 = to_dev(kcl), to_dev(vcl)
+        del kcl, vcl
+        copies_l = [(tkl0, tvl0)] + [(tkl0.clone(), tvl0.clone())
+                                     for _ in range(args.decode_copies - 1)]
+        tll, tsl = torch.from_numpy(lens_l).to(dev), torch.from_numpy(starts_l).to(dev)
+        ol = torch.empty_like(tql)
+        opts_l = opts_of(wl)
+        cfg_l = bd.make_decode_cfg(wl.B, wl.Hq, wl.Hkv, wl.D, wl.T, opts_l)
+        wsl = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg_l))),
+                          dtype=torch.uint8, device=dev)
+
+        def dec_l(i):
+            kcc, vcc = copies_l[i % len(copies_l)]
+            bd.attn_decode(tql, kcc, vcc, tll, opts_l, out=ol, workspace=wsl, cache_start=tsl)
+
+        for i in range(10):
+            dec_l(i)
+        torch.cuda.synchronize()
+        evl = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evl[0].record(stream)
+        for i in range(n):
+            dec_l(i)
+        evl[1].record(stream)
+        torch.cuda.synchronize()
+        ms_l = evl[0].elapsed_time(evl[1]) / n
+        gbs_l = decode_bytes(wl, lens_l - starts_l) / (ms_l * 1e-3) / 1e9
+        extra[wl.name] = dict(us_per_call=ms_l * 1e3, GBps=gbs_l,
+                              pct_hbm_peak=100 * gbs_l / PEAK_HBM_GBS)
+        log(f"[bench] {wl.name}: {ms_l * 1e3:.1f} us/call  {gbs_l:.0f} GB/s")
+        del copies_l, tkl0, tvl0
+        torch.cuda.empty_cache()
         # Multi-token step (append + attend) on decode-sized caches.
         we = WORKLOADS["gqa181m_extend"]
         qe, kne, vne, kce, vce, lens_e = make_extend_inputs(we)
