@@ -230,6 +230,12 @@ def main():
                     dropout=w.dropout, kernels_ms={n: round(a, 4) for n, a in ktimes.items()},
                     mask_gdecisions_per_s=tiles * 1024 / (ktimes["dropout_mask"] * 1e-3) / 1e9)
             log(f"[bench] {name}: {ms2:.3f} ms/step  {tf2:.1f} TFLOP/s")
+        # flaxchat's layer pattern: three sliding-window layers per global one.
+        wf, ww = WORKLOADS["flaxchat_full"], WORKLOADS["flaxchat_w512"]
+        ms_mix = (3 * extra["flaxchat_w512"]["ms_per_step"] + extra["flaxchat_full"]["ms_per_step"]) / 4
+        tf_mix = (3 * train_flops(ww) + train_flops(wf)) / 4 / (ms_mix * 1e-3) / 1e12
+        extra["flaxchat_sssl_mix"] = dict(ms_per_layer=ms_mix, tflops=tf_mix,
+                                          pct_peak=100 * tf_mix / PEAK_BF16_TFLOPS)
         # SFT-style packed rows (segment ids) on the 181M shapes.
         wp = WORKLOADS["gqa181m_sft_packed"]
         ids = make_segment_ids(wp)
@@ -416,6 +422,23 @@ def main():
                "sample": f"{units} (batch, KV-group) slices of {w.name} (1 x {G} query heads x "
                          f"T={w.T} x d={w.D}) fwd+bwd in {el:.1f} s, host os.cpu_count()="
                          f"{os.cpu_count()}"}
+        # The same oracle on one core, on a third of the time.
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                t0, n1 = time.perf_counter(), 0
+                while time.perf_counter() - t0 < args.cpu_seconds / 3:
+                    b, g = n1 % w.B, (n1 // w.B) % w.Hkv
+                    hs = slice(g * G, (g + 1) * G)
+                    attention_forward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], **kw)
+                    attention_backward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                                       dO[b:b + 1, hs], **kw)
+                    n1 += 1
+                el1 = time.perf_counter() - t0
+            cpu["single_core"] = {"value": train_flops(w.with_(B=1, Hq=G, Hkv=1)) * n1 / el1 / 1e12,
+                                  "unit": "TFLOP/s", "sample": f"{n1} slices in {el1:.1f} s"}
+        except Exception as e:  # threadpoolctl missing: report the multi-core figure only
+            cpu["single_core"] = {"error": str(e)}
         log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s over {units} slices")
 
     line = {
