@@ -8,9 +8,10 @@
 //
 // The work is HBM-bound (about 2 flops per byte), so it runs on the vector ALUs with
 // coalesced 16-byte loads, not on MFMA:
-//  * split kernel: one workgroup per (chunk of split_len cache rows, b, kv head, head
-//    subset).  Four lanes share one row (each owns D/4 elements: 64 contiguous bytes per
-//    quad and load); a wave covers 16 rows per step, and the chunk is streamed in passes
+//  * split kernel: one 4-wave workgroup per (chunk of split_len cache rows, b, kv head, head
+//    subset), two resident per CU.  Four lanes share one row (each owns D/4 elements: 64
+//    contiguous bytes per quad and load); a wave covers 16 rows per step, and the chunk is
+//    streamed in passes
 //    through a two-stage register pipeline (the loads of the next pass are in flight while
 //    the current one computes).  Each quad keeps a running (max, sum, output) for every
 //    query head of the GQA group (K and V are read once per KV head); quads and waves are
@@ -47,7 +48,9 @@ __device__ __forceinline__ int active_first(const DecArgs& a, int b, int L) {
   return a.cache_start ? min(max(a.cache_start[b], 0), L) : 0;
 }
 
-constexpr int kDecWaves = 8;  // waves per split workgroup
+// Waves per split workgroup: four, with two workgroups resident per CU, so one streams while
+// the other starts up or drains (measured faster than one 8-wave workgroup per CU).
+constexpr int kDecWaves = 4;
 // Largest factor a running maximum may grow by before the accumulators are rescaled (log2).
 constexpr float kRescaleSlack = 8.f;
 
@@ -114,7 +117,7 @@ __device__ __forceinline__ void merge_quads(RunState<NE>& s) {
 }
 
 template <int D, int HPB, int MODE>
-__global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs a) {
   constexpr int NW = kDecWaves;
   constexpr int NU = D / 32;      // 16-byte chunks per lane per row
   constexpr int NE = NU * 8;      // output elements per lane and head
@@ -386,9 +389,16 @@ hipError_t launch_split_mode(const DecArgs& a, int mode, hipStream_t s) {
 template <int D>
 hipError_t launch_decode_d(const DecArgs& a, int mode, hipStream_t s) {
   hipError_t e;
+  // decode_heads_per_block keeps heads x D <= 256, so only those instantiations exist.
   switch (decode_heads_per_block(a.Hq / a.Hkv, D)) {
-    case 4: e = launch_split_mode<D, 4>(a, mode, s); break;
-    case 3: e = launch_split_mode<D, 3>(a, mode, s); break;
+    case 4:
+      if constexpr (4 * D <= 256) e = launch_split_mode<D, 4>(a, mode, s);
+      else e = hipErrorInvalidValue;
+      break;
+    case 3:
+      if constexpr (3 * D <= 256) e = launch_split_mode<D, 3>(a, mode, s);
+      else e = hipErrorInvalidValue;
+      break;
     case 2: e = launch_split_mode<D, 2>(a, mode, s); break;
     default: e = launch_split_mode<D, 1>(a, mode, s); break;
   }
