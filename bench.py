@@ -126,6 +126,40 @@ def main():
     # ------------------------------------------------------------------------------------
     # fwd + bwd
     # ------------------------------------------------------------------------------------
+    def timed(fn, n):
+        """Milliseconds for n back-to-back calls of fn: one HIP event pair on the launch stream
+        around all of them, synchronised on both sides (no marker between the calls)."""
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def per_call_ms(fn, n):
+        """Per-call times from an event after every call (a separate pass: the markers between
+        calls add their own cost, so these are for the spread, not the rate)."""
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
+            fn(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+
+    def settle(fn, seconds=0.5):
+        """Run fn back to back for `seconds` before any warm-up or timing: a cold GPU takes some
+        tens of milliseconds of load to reach its steady clocks, and the first workload timed
+        would otherwise run partly below them.  Untimed."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for i in range(4):
+                fn(i)
+            torch.cuda.synchronize()
+
     def train_case(w, steps, warmup, trace=False, ids=None):
         """Time fwd + bwd; with w.dropout > 0 each step also draws a fresh keep mask."""
         q, k, v, dO = make_train_inputs(w)
@@ -153,27 +187,24 @@ def main():
             nm = bd.lib().attn_dropout_mask_bytes(ctypes.byref(cfg))
             mask = torch.empty(max(int(nm), 1), dtype=torch.uint8, device=dev)
         calls = [0]
+        # The backward takes k after RoPE / QK-norm from the forward's workspace (a training
+        # step keeps it from the forward to the backward, as it keeps o and lse).
+        khat = wsf if ((w.rope or w.qk_norm) and tids is None and mask is None) else None
 
-        def step():
+        def step(_i=0):
             if mask is not None:
                 bd.attn_dropout_mask(tq, tk, p, w.seed, calls[0], opts, out=mask)
                 calls[0] += 1
             bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf, segment_ids=tids,
                         dropout_p=p, dropout_mask=mask)
             bd.attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb,
-                        segment_ids=tids, dropout_p=p, dropout_mask=mask)
+                        segment_ids=tids, dropout_p=p, dropout_mask=mask, khat=khat)
 
+        settle(step)
         for _ in range(warmup):
             step()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record(stream)
-        for i in range(steps):
-            step()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-        total_ms = ev[0].elapsed_time(ev[steps])
+        total_ms = timed(step, steps)
+        per = per_call_ms(step, steps)
         kern = None
         if trace:
             bd.trace_enable(True)
@@ -193,8 +224,8 @@ def main():
         flops = train_flops(main_w)
         tflops = flops / (ms * 1e-3) / 1e12
         result.update(value=tflops, ms_per_step=ms)
-        extra["gqa181m_train"] = dict(ms_median=float(np.median(per)),
-                                      ms_p90=float(np.percentile(per, 90)),
+        extra["gqa181m_train"] = dict(marker_ms_median=float(np.median(per)),
+                                      marker_ms_p90=float(np.percentile(per, 90)),
                                       tflops=tflops, pct_peak=100 * tflops / PEAK_BF16_TFLOPS)
         log(f"[bench] {main_w.name}: {ms:.3f} ms/step  {tflops:.1f} TFLOP/s")
         # Dominant kernel and its algorithmic rate.
@@ -219,7 +250,7 @@ def main():
             drop = w.dropout > 0
             ms2, per2, k2 = train_case(w, max(args.steps // 2, 3), 2, trace=drop)
             tf2 = train_flops(w) / (ms2 * 1e-3) / 1e12
-            extra[name] = dict(ms_per_step=ms2, ms_median=float(np.median(per2)), tflops=tf2,
+            extra[name] = dict(ms_per_step=ms2, marker_ms_median=float(np.median(per2)), tflops=tf2,
                                pct_peak=100 * tf2 / PEAK_BF16_TFLOPS)
             if drop:
                 # The mask kernel is integer-ALU work: report its rate in keep decisions per second
@@ -242,7 +273,7 @@ def main():
         log(f"[bench] fwd+bwd {wp.name}")
         msp, perp, _ = train_case(wp, max(args.steps // 2, 3), 2, ids=ids)
         tfp = packed_flops(wp, ids) / (msp * 1e-3) / 1e12
-        extra[wp.name] = dict(ms_per_step=msp, ms_median=float(np.median(perp)), tflops=tfp,
+        extra[wp.name] = dict(ms_per_step=msp, marker_ms_median=float(np.median(perp)), tflops=tfp,
                               pct_peak=100 * tfp / PEAK_BF16_TFLOPS)
         log(f"[bench] {wp.name}: {msp:.3f} ms/step  {tfp:.1f} TFLOP/s")
         torch.cuda.empty_cache()
@@ -276,20 +307,18 @@ def main():
         cfg = bd.make_decode_cfg(wd.B, wd.Hq, wd.Hkv, wd.D, wd.T, opts)
         wsd = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg))),
                           dtype=torch.uint8, device=dev)
-        for i in range(10):
-            kcc, vcc = copies[i % len(copies)]
-            bd.attn_decode(tq, kcc, vcc, tl, opts, out=od, workspace=wsd)
-        torch.cuda.synchronize()
         n = args.decode_iters
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        ev[0].record(stream)
-        for i in range(n):
+
+        def dec(i):
             kcc, vcc = copies[i % len(copies)]
             bd.attn_decode(tq, kcc, vcc, tl, opts, out=od, workspace=wsd)
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
-        ms_d = ev[0].elapsed_time(ev[n]) / n
+
+        settle(dec)
+        for i in range(10):
+            dec(i)
+
+        ms_d = timed(dec, n) / n
+        per = per_call_ms(dec, n)
         nbytes = decode_bytes(wd, lens)
         gbs = nbytes / (ms_d * 1e-3) / 1e9
         bd.trace_enable(True)
@@ -300,8 +329,8 @@ def main():
         dk = bd.trace_read()
         bd.trace_enable(False)
         split = {k: round(t / c, 5) for k, (c, t) in dk.items()}
-        extra["decode"] = dict(ms_per_call=ms_d, ms_median=float(np.median(per)),
-                               ms_p90=float(np.percentile(per, 90)), GBps=gbs,
+        extra["decode"] = dict(ms_per_call=ms_d, marker_ms_median=float(np.median(per)),
+                               marker_ms_p90=float(np.percentile(per, 90)), GBps=gbs,
                                pct_hbm_peak=100 * gbs / PEAK_HBM_GBS, bytes_per_call=nbytes,
                                kernels_ms=split)
         log(f"[bench] decode: {ms_d * 1e3:.1f} us/call  {gbs:.0f} GB/s")

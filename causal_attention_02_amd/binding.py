@@ -24,6 +24,7 @@ EXPORTED = [
     "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
     "attn_trace_enable", "attn_trace_read", "attn_dropout_mask_bytes", "attn_dropout_mask",
     "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_leftpad", "attn_extend_leftpad",
+    "attn_bwd_khat",
 ]
 
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_fwd.restype = ctypes.c_int
         L.attn_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_bwd_khat.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_bwd_khat.restype = ctypes.c_int
         L.attn_bwd.restype = ctypes.c_int
         L.attn_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_fwd_packed.restype = ctypes.c_int
@@ -302,9 +305,13 @@ def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, wo
 
 
 def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, segment_ids=None, dropout_p=0.0, dropout_mask=None):
+             workspace=None, stream=None, segment_ids=None, dropout_p=0.0, dropout_mask=None,
+             khat=None):
     """Backward (bf16): returns (dq, dk, dv) with respect to the raw q, k, v (packed rows with
-    segment_ids, dropout with the forward's dropout_mask and dropout_p, as in attn_fwd)."""
+    segment_ids, dropout with the forward's dropout_mask and dropout_p, as in attn_fwd).
+
+    khat (optional): the forward's workspace (or any buffer starting with k after RoPE /
+    QK-norm, bf16 [B,Hkv,T,D]); the backward then skips its own pass over k."""
     torch = _torch()
     opts = opts or AttnOptions()
     B, Hq, T, D = q.shape
@@ -322,6 +329,17 @@ def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, d
     _need(dv, v.shape, bf, "dv")
     cfg = make_cfg(B, T, Hq, Hkv, D, opts, ATTN_BF16)
     _check(lib().attn_check_cfg(ctypes.byref(cfg), 1), "attn_bwd")
+    if khat is not None:
+        if segment_ids is not None or dropout_mask is not None:
+            raise ValueError("khat is taken by the plain backward only")
+        if _nbytes(khat) < B * Hkv * T * D * 2 or not khat.is_cuda or not khat.is_contiguous():
+            raise ValueError("khat: need a contiguous GPU buffer of k's bf16 size")
+        ws = _workspace(int(lib().attn_bwd_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+        st = lib().attn_bwd_khat(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                                 _ptr(lse), _ptr(khat), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                 ctypes.c_size_t(_nbytes(ws)), _stream(stream))
+        _check(st, "attn_bwd_khat")
+        return dq, dk, dv
     if dropout_mask is not None:
         if segment_ids is not None:
             raise ValueError("dropout with segment ids is not supported")

@@ -284,10 +284,12 @@ static int fwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
   return launch_status(e);
 }
 
+// khat: k after RoPE / QK-norm as the forward used it (null: computed here).
 static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void* v,
                     const void* o, const void* dO, const float* lse, const int32_t* ids,
                     void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
-                    const void* drop = nullptr, float dscale = 1.f) {
+                    const void* drop = nullptr, float dscale = 1.f,
+                    const void* khat = nullptr) {
   int st = check_cfg(c, 1);
   if (st != ATTN_OK) return st;
   if (c->B == 0 || c->T == 0) return ATTN_OK;
@@ -308,10 +310,14 @@ static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
   if (pro) {
     qh = w;
     w += align_up((size_t)qrows * c->D * 2);
-    void* kw = w;
-    e = launch_prologue(k, kw, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
-                        c->norm_eps, s);
-    kh = kw;
+    if (khat) {
+      kh = khat;
+    } else {
+      void* kw = w;
+      e = launch_prologue(k, kw, krows, c->T, c->D, 2, c->rope, c->rope_base, c->qk_norm,
+                          c->norm_eps, s);
+      kh = kw;
+    }
   }
   BwdParams p{q, k, kh, qh, v, o, dO, lse, Dvec, L2, dq, dk, dv, c->B, c->T, c->Hq, c->Hkv, c->D,
               c->window, eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base,
@@ -342,6 +348,14 @@ int attn_bwd(const attn_cfg* c, const void* q, const void* k, const void* v, con
              const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
              size_t ws_bytes, void* stream) {
   return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+int attn_bwd_khat(const attn_cfg* c, const void* q, const void* k, const void* v, const void* o,
+                  const void* dO, const float* lse, const void* khat, void* dq, void* dk,
+                  void* dv, void* ws, size_t ws_bytes, void* stream) {
+  if (c && (c->rope || c->qk_norm) && c->B > 0 && c->T > 0 && !khat) return ATTN_EINVAL;
+  return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream, nullptr,
+                  1.f, khat);
 }
 
 int attn_fwd_packed(const attn_cfg* c, const void* q, const void* k, const void* v,

@@ -139,6 +139,17 @@ int attn_bwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, c
              size_t ws_bytes, void* stream);
 
 /*
+ * attn_bwd_khat -- attn_bwd without its own pass over k: khat is k after RoPE / QK-norm,
+ * bf16 [B, Hkv, T, D], exactly as the forward used it.  A bfloat16 attn_fwd with RoPE or
+ * QK-norm on leaves it at the start of its workspace, so a caller that keeps that workspace
+ * from the forward to the backward passes it here (every other argument as for attn_bwd).
+ * With neither RoPE nor QK-norm khat is not read (k is used) and may be NULL.
+ */
+int attn_bwd_khat(const attn_cfg* cfg, const void* q, const void* k, const void* v,
+                  const void* o, const void* dO, const float* lse, const void* khat, void* dq,
+                  void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * attn_fwd_packed, attn_bwd_packed -- attn_fwd / attn_bwd for rows that pack several
  * sequences (the nanoGPT-JAX 181M model card's SFT data: rows packed with segment ids).
  *   segment_ids [B, T] device, int32 -- a segment is a maximal run of equal ids in a row;

@@ -173,6 +173,22 @@ def test_leftpad_entry_points_validation(L):
                                  s) == 0
 
 
+def test_bwd_khat_validation(L):
+    fake, null, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0), ctypes.c_void_p(0)
+    c = cfg()  # RoPE and QK-norm on: khat is required
+    need = L.attn_bwd_workspace_bytes(ctypes.byref(c))
+    assert L.attn_bwd_khat(ctypes.byref(c), fake, fake, fake, fake, fake, fake, null, fake, fake,
+                           fake, fake, need, s) == -1
+    assert L.attn_bwd_khat(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                           fake, fake, need - 1, s) == -3
+    plain = cfg(opts=bd.AttnOptions())  # neither: khat unused, the usual checks apply
+    assert L.attn_bwd_khat(ctypes.byref(plain), fake, fake, fake, fake, fake, fake, null, null,
+                           fake, fake, fake, 1 << 40, s) == -1
+    empty = cfg(T=0)
+    assert L.attn_bwd_khat(ctypes.byref(empty), null, null, null, null, null, null, null, null,
+                           null, null, null, 0, s) == 0
+
+
 def test_decode_config_validation(L):
     o = bd.AttnOptions(softcap=50.0, rope=True)
     assert L.attn_check_decode_cfg(ctypes.byref(bd.make_decode_cfg(64, 8, 4, 96, 2048, o))) == 0

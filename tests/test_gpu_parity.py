@@ -184,6 +184,27 @@ def test_full_size_sampled(name):
         check_bf16(w, sl, ref_f, ref_b, f"{name}[b={b},g={g}]")
 
 
+def test_bwd_khat_equals_bwd():
+    """attn_bwd with the forward's k^ (the start of its workspace) gives attn_bwd's gradients
+    bitwise, for the RoPE/QK-norm workloads and for plain attention (khat unused)."""
+    import torch
+    from causal_attention_02_amd import fwd_workspace_bytes
+    for w in (WORKLOADS["gqa181m_train"].with_(B=2, T=333),
+              WORKLOADS["flaxchat_w512"].with_(B=1, T=700),
+              Workload("plain_khat", B=2, T=130, Hq=4, Hkv=2, D=64)):
+        q, k, v, dO = make_train_inputs(w)
+        tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+        wsf = torch.empty(max(fwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, opts_of(w)), 1),
+                          dtype=torch.uint8, device="cuda")
+        o, lse = attn_fwd(tq, tk, tv, opts_of(w), workspace=wsf)
+        ref = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))
+        got = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w),
+                       khat=wsf if (w.rope or w.qk_norm) else tk)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), w.name
+
+
 def test_backward_is_deterministic():
     import torch
     w = WORKLOADS["gqa181m_train"].with_(B=2, T=512)
@@ -712,6 +733,72 @@ def test_leftpad_prefill_then_decode_matches_forward():
     od = attn_decode(tq[:, :, -1].contiguous(), kc, vc, full, opts_of(w), cache_start=ts)
     torch.cuda.synchronize()
     assert rel_l2(to_host(od), o[:, :, -1]) <= 1e-2
+
+
+# --------------------------------------------------------------------------------------------
+# HIP graph capture: the library only enqueues kernels on the given stream (no allocation, no
+# memset, no synchronisation), so a training step or a decode step records into a graph.
+# --------------------------------------------------------------------------------------------
+def test_graph_replay_matches_eager():
+    """fwd + bwd, dropout (mask + fwd + bwd) and decode captured in one torch.cuda.CUDAGraph on
+    torch's current stream; every replay, with eager work and synchronisation between replays,
+    reproduces the eager results bitwise."""
+    import torch
+    from causal_attention_02_amd import bwd_workspace_bytes, fwd_workspace_bytes
+    w = WORKLOADS["gqa181m_train"].with_(B=2, T=300)
+    q, k, v, dO = make_train_inputs(w)
+    tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+    opts = opts_of(w)
+    B, Hq, T, D, Hkv = w.B, w.Hq, w.T, w.D, w.Hkv
+    o, lse = torch.empty_like(tq), torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    wsf = torch.empty(max(fwd_workspace_bytes(B, T, Hq, Hkv, D, opts), 1), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(max(bwd_workspace_bytes(B, T, Hq, Hkv, D, opts), 1), dtype=torch.uint8,
+                      device="cuda")
+    mask = attn_dropout_mask(tq, tk, 0.1, 7, 0, opts)
+    wd = WORKLOADS["gqa181m_decode"].with_(B=5, T=700)
+    qd, kc, vc, lens = make_decode_inputs(wd)
+    lens[:] = [0, 1, 300, 700, 650]
+    tqd, tkc, tvc = (to_dev(x, torch.bfloat16) for x in (qd, kc, vc))
+    tl = torch.from_numpy(lens).to("cuda")
+    od = torch.empty_like(tqd)
+    dec_ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+
+    def step():
+        attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf)
+        attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb)
+        attn_dropout_mask(tq, tk, 0.1, 7, 1, opts, out=mask)
+        attn_fwd(tq, tk, tv, opts, out=o2, lse=lse2, workspace=wsf, dropout_p=0.1,
+                 dropout_mask=mask)
+        attn_bwd(tq, tk, tv, o2, tdo, lse2, opts, dq=dq2, dk=dk2, dv=dv2, workspace=wsb,
+                 dropout_p=0.1, dropout_mask=mask)
+        attn_decode(tqd, tkc, tvc, tl, opts_of(wd), split_len=128, out=od, workspace=dec_ws)
+
+    outs = (o, lse, dq, dk, dv, o2, lse2, dq2, dk2, dv2, od)
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for x in outs:
+            x.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), (rep, i)
+    _say("graph replays match the eager step")
 
 
 def test_errors_on_gpu():
