@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   const int qt = a.ntiles - 1 - rank;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int q0 = qt * kBMq, qw0 = q0 + 32 * w;
   const int qi = qw0 + lr;
   const int qrow = min(qi, T - 1);
@@ -212,10 +213,132 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  // One key tile: S^T = K q^T and dP^T = V dO^T for both 32-key blocks (dP^T accumulates on
-  // top of -D_i, so it comes out as dP - D), then per half block dS and dQ^T += K^T dS^T.
-  // The phase fences keep one phase's registers live at a time (two waves share a SIMD).
-  auto run = [&](int kt, const bf16* sk, const bf16* sv, const uint32_t* sm) {
+  // One key tile, two 32-key blocks.  For each block: S^T = K q^T and dP^T = V dO^T, then
+  // dS = P (dP - D) and dQ^T += K^T dS^T.
+  // The wave's instruction stream pairs the matrix work of one block with the elementwise
+  // work of the other, so the wave keeps its matrix and vector units busy at once: block 0's
+  // products; block 1's products beside block 0's dS; block 0's dQ products beside block 1's
+  // dS; block 1's dQ products.
+  auto run_paired = [&](int kt, const bf16* sk, const bf16* sv,
+                      const uint32_t* sm) __attribute__((always_inline)) {
+    const int k0 = kt * kBNk;
+    const bool skip = !wave_active || k0 > qw_last || k0 + kBNk - 1 < s_lo ||
+                      (window > 0 && k0 + kBNk - 1 < qw0 - window + 1);
+    if (skip) return;
+    uint32_t mw[2] = {0u, 0u};
+    if constexpr (DROP) {
+      mw[0] = sm[qi - q0] >> (4 * gl);
+      mw[1] = sm[kBMq + qi - q0] >> (4 * gl);
+    }
+    const bool need_mask = (k0 + kBNk - 1 > qw0) || k0 < s_hi ||
+                           (window > 0 && k0 < qw_last - window + 1);
+    // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
+    const int qd = qi - k0 - 4 * gl;
+
+    auto body = [&](auto masked) {
+      f32x16 sacc[2], pacc[2];
+      bf16x8 dsb[2][2];
+      // dS for element r of block kb, in place of its score.
+      auto grad = [&](int kb, int r) {
+        float gf;
+        float y = score_grad<MODE>(sacc[kb][r], a.sc, lse2, &gf);
+        if constexpr (decltype(masked)::value)
+          y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
+        float p = exp2_fast(y);
+        if constexpr (MODE != kScoreScale) p *= gf;
+        if constexpr (DROP)
+          sacc[kb][r] = p * fmaf(keep_only(a.drop_scale, mw[kb], r), pacc[kb][r], -Di);
+        else
+          sacc[kb][r] = p * (pacc[kb][r] - Di);
+        // Pins the element's arithmetic to the step that asks for it (the scheduling fences
+        // alone leave free arithmetic to drift towards its first use).
+        asm volatile("" : "+v"(sacc[kb][r]));
+      };
+      auto kv_off = [&](int kb, int s) { return (kb * 32 + lr) * LD + 16 * s + 8 * gl; };
+      auto kt_ptr = [&](int kb, int i) {  // step i = NDB t + db of block kb's dQ products
+        return sk + (kb * 32 + 16 * (i / NDB) + trow) * LD + 32 * (i % NDB) + tcol;
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[kb][r] = 0.f;  // zero accumulators need no vector instructions before the MFMA
+          pacc[kb][r] = 0.f;
+        }
+      // Block 0's products, scheduled by the compiler.
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 ka = ld16<bf16x8>(sk + kv_off(0, s));
+        const bf16x8 va = ld16<bf16x8>(sv + kv_off(0, s));
+        sacc[0] = mfma32(ka, bq[s], sacc[0]);
+        pacc[0] = mfma32(va, bdo[s], pacc[0]);
+      }
+      // Operand reads run PF steps ahead of their MFMAs (one where dropout's keep words leave
+      // no registers for a second set).
+      constexpr int PF = (DROP && D >= 96) ? 1 : 2;
+      bf16x8 ka[PF], va[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) {
+        ka[s] = ld16<bf16x8>(sk + kv_off(1, s));
+        va[s] = ld16<bf16x8>(sv + kv_off(1, s));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Block 1's products, each pair followed by a later pair's operand reads and a share of
+      // block 0's dS.
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc[1] = mfma32(ka[s % PF], bq[s], sacc[1]);
+        pacc[1] = mfma32(va[s % PF], bdo[s], pacc[1]);
+        if (s + PF < NS) {
+          ka[s % PF] = ld16<bf16x8>(sk + kv_off(1, s + PF));
+          va[s % PF] = ld16<bf16x8>(sv + kv_off(1, s + PF));
+        }
+#pragma unroll
+        for (int r = 16 * s / NS; r < 16 * (s + 1) / NS; ++r) grad(0, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dsb[0][0] = pack8(sacc[0], 0);
+      dsb[0][1] = pack8(sacc[0], 8);
+      bf16x8 kt_[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) kt_[i] = tr_read_pair(kt_ptr(0, i), kt_ptr(0, i) + 8 * LD);
+      __builtin_amdgcn_sched_barrier(0);
+      // Block 0's dQ products, each followed by a later operand's reads and a share of
+      // block 1's dS.
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) {
+        dqacc[i % NDB] = mfma32(kt_[i % PF], dsb[0][i / NDB], dqacc[i % NDB]);
+        if (i + PF < 2 * NDB)
+          kt_[i % PF] = tr_read_pair(kt_ptr(0, i + PF), kt_ptr(0, i + PF) + 8 * LD);
+#pragma unroll
+        for (int r = 16 * i / (2 * NDB); r < 16 * (i + 1) / (2 * NDB); ++r) grad(1, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dsb[1][0] = pack8(sacc[1], 0);
+      dsb[1][1] = pack8(sacc[1], 8);
+      // Block 1's dQ products.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 kr[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          kr[db] = tr_read_pair(kt_ptr(1, NDB * t + db), kt_ptr(1, NDB * t + db) + 8 * LD);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(kr[db], dsb[1][t], dqacc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (need_mask)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  };
+
+  // The same tile in phases: S^T and dP^T for both blocks (dP^T accumulates on top of -D_i,
+  // so it comes out as dP - D), then per half block dS and dQ^T += K^T dS^T.  The phase
+  // fences keep one phase's registers live at a time.
+  auto run_phased = [&](int kt, const bf16* sk, const bf16* sv,
+                      const uint32_t* sm) __attribute__((always_inline)) {
     const int k0 = kt * kBNk;
     const bool skip = !wave_active || k0 > qw_last || k0 + kBNk - 1 < s_lo ||
                       (window > 0 && k0 + kBNk - 1 < qw0 - window + 1);
@@ -287,6 +410,16 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
     }
   };
 
+  // The paired order holds about twenty more registers than the phased one; at d = 128
+  // without a soft-cap (two waves per SIMD, 256 registers each) that would spill.
+  auto run = [&](int kt, const bf16* sk, const bf16* sv,
+               const uint32_t* sm) __attribute__((always_inline)) {
+    if constexpr (D >= 128 && MODE == kScoreScale)
+      run_phased(kt, sk, sv, sm);
+    else
+      run_paired(kt, sk, sv, sm);
+  };
+
   // Two-deep pipeline over key tiles, unrolled by two so each LDS buffer is a distinct
   // array: the loads into one buffer never wait on reads of the other.
   dma(kt0, 0);
@@ -339,7 +472,8 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
   const int bg = blockIdx.x - kt * nbg;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int w = tid >> 6;
   const int kwg0 = kt * kBNkv;
   const int kw0 = kwg0 + 32 * w;
   const int kj = kw0 + lr;
@@ -468,60 +602,145 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
       // Phase fences: with two waves per SIMD the other wave fills one wave's MFMA, VALU
       // and LDS phases, so each wave keeps only one phase's registers live.
       __builtin_amdgcn_sched_barrier(0);
-      // Half t covers elements 8t .. 8t + 7 (queries 16t .. 16t + 15 of the block): the
-      // softmax gradient, then that half's share of dV^T += dO^T P and dK^T += q^T dS.
+      // The exp-form soft-cap's gradient holds a few more registers; at d >= 96 pairing the
+      // halves would spill, so there they run one after the other.
+      if constexpr (MODE != kScoreCapExp || D < 96) {
+        // Half t covers elements 8t .. 8t + 7 (queries 16t .. 16t + 15 of the block): the
+        // softmax gradient, then that half's share of dV^T += dO^T P and dK^T += q^T dS.  Half
+        // 0's products are issued beside half 1's gradient, so the wave's matrix and vector
+        // units work at once.
+        float4 lq[2][2], nq[2][2];  // LSE and -D (dropout only) of each half's queries
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float4 lq[2] = {*reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t),
-                              *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t + 8)};
-        float4 nq[2];  // -D of the half's queries (dropout: dP starts at 0)
-        if constexpr (DROP) {
-          nq[0] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t);
-          nq[1] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t + 8);
-        }
-        auto grads = [&](auto masked) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * t + e;
-            const int qo = 8 * (r >> 2) + (r & 3);
-            float gf;
-            float y = score_grad<MODE>(sacc[r], a.sc, lq[e >> 2][e & 3], &gf);
-            if constexpr (decltype(masked)::value)
-              y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
-            const float p = exp2_fast(y);
-            float ds;
-            if constexpr (DROP) {
-              const float4 n4 = nq[e >> 2];
-              const float nd = (e & 3) == 0 ? n4.x : (e & 3) == 1 ? n4.y : (e & 3) == 2 ? n4.z : n4.w;
-              ds = p * fmaf(keep_only(a.drop_scale, mw, r), pacc[r], nd);
-              sacc[r] = keep_only(p, mw, r);  // dV takes the kept weights; scaled at the end
-            } else {
-              ds = p * pacc[r];
-              sacc[r] = p;
-            }
-            if constexpr (MODE != kScoreScale) ds *= gf;
-            pacc[r] = ds;
+          for (int j = 0; j < 2; ++j) {
+            lq[t][j] = *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * t + 8 * j);
+            if constexpr (DROP)
+              nq[t][j] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t + 8 * j);
           }
+        auto grad = [&](auto masked, int r) {
+          const int t = r >> 3, e = r & 7;
+          const int qo = 8 * (r >> 2) + (r & 3);
+          const float4 l4 = lq[t][e >> 2];
+          const float lse = (e & 3) == 0 ? l4.x : (e & 3) == 1 ? l4.y : (e & 3) == 2 ? l4.z : l4.w;
+          float gf;
+          float y = score_grad<MODE>(sacc[r], a.sc, lse, &gf);
+          if constexpr (decltype(masked)::value) y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
+          const float p = exp2_fast(y);
+          float ds;
+          if constexpr (DROP) {
+            const float4 n4 = nq[t][e >> 2];
+            const float nd = (e & 3) == 0 ? n4.x : (e & 3) == 1 ? n4.y : (e & 3) == 2 ? n4.z : n4.w;
+            ds = p * fmaf(keep_only(a.drop_scale, mw, r), pacc[r], nd);
+            sacc[r] = keep_only(p, mw, r);  // dV takes the kept weights; scaled at the end
+          } else {
+            ds = p * pacc[r];
+            sacc[r] = p;
+          }
+          if constexpr (MODE != kScoreScale) ds *= gf;
+          pacc[r] = ds;
+          // Pins the element's arithmetic to the step that asks for it.
+          asm volatile("" : "+v"(sacc[r]), "+v"(pacc[r]));
+        };
+        auto tr_off = [&](int i) {  // product step i = NDB t + db
+          return (qb * 32 + 16 * (i / NDB) + trow) * LD + 32 * (i % NDB) + tcol;
+        };
+        auto half = [&](auto masked) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) grad(masked, r);
+          bf16x8 pb[2], dsb[2];
+          pb[0] = pack8(sacc, 0);
+          dsb[0] = pack8(pacc, 0);
+          bf16x8 ot = tr_read_pair(so + tr_off(0), so + tr_off(0) + 8 * LD);
+          bf16x8 qt_ = tr_read_pair(sq + tr_off(0), sq + tr_off(0) + 8 * LD);
+          __builtin_amdgcn_sched_barrier(0);
+          // Half 0's products, each followed by the next operands' reads and a share of half
+          // 1's gradient; then half 1's products.
+#pragma unroll
+          for (int i = 0; i < NDB; ++i) {
+            dvacc[i] = mfma32(ot, pb[0], dvacc[i]);
+            dkacc[i] = mfma32(qt_, dsb[0], dkacc[i]);
+            ot = tr_read_pair(so + tr_off(i + 1), so + tr_off(i + 1) + 8 * LD);
+            qt_ = tr_read_pair(sq + tr_off(i + 1), sq + tr_off(i + 1) + 8 * LD);
+#pragma unroll
+            for (int r = 8 + 8 * i / NDB; r < 8 + 8 * (i + 1) / NDB; ++r) grad(masked, r);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          pb[1] = pack8(sacc, 8);
+          dsb[1] = pack8(pacc, 8);
+#pragma unroll
+          for (int i = NDB; i < 2 * NDB; ++i) {
+            dvacc[i - NDB] = mfma32(ot, pb[1], dvacc[i - NDB]);
+            dkacc[i - NDB] = mfma32(qt_, dsb[1], dkacc[i - NDB]);
+            if (i + 1 < 2 * NDB) {
+              ot = tr_read_pair(so + tr_off(i + 1), so + tr_off(i + 1) + 8 * LD);
+              qt_ = tr_read_pair(sq + tr_off(i + 1), sq + tr_off(i + 1) + 8 * LD);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         };
         if (need_mask)
-          grads(std::true_type{});
+          half(std::true_type{});
         else
-          grads(std::false_type{});
-        const bf16x8 pb = pack8(sacc, 8 * t), dsb = pack8(pacc, 8 * t);
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 ot[NDB], qt_[NDB];
+          half(std::false_type{});
+      } else {
+        // Half t covers elements 8t .. 8t + 7 (queries 16t .. 16t + 15 of the block): the
+        // softmax gradient, then that half's share of dV^T += dO^T P and dK^T += q^T dS.
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int off = (qb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
-          ot[db] = tr_read_pair(so + off, so + off + 8 * LD);
-          qt_[db] = tr_read_pair(sq + off, sq + off + 8 * LD);
-        }
+        for (int t = 0; t < 2; ++t) {
+          const float* lrow = sl + qb * 32 + 4 * gl + 16 * t;
+          const float4 lq[2] = {*reinterpret_cast<const float4*>(lrow),
+                                *reinterpret_cast<const float4*>(lrow + 8)};
+          float4 nq[2];  // -D of the half's queries (dropout: dP starts at 0)
+          if constexpr (DROP) {
+            nq[0] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t);
+            nq[1] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 16 * t + 8);
+          }
+          auto grads = [&](auto masked) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = mfma32(ot[db], pb, dvacc[db]);
-          dkacc[db] = mfma32(qt_[db], dsb, dkacc[db]);
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * t + e;
+              const int qo = 8 * (r >> 2) + (r & 3);
+              float gf;
+              float y = score_grad<MODE>(sacc[r], a.sc, lq[e >> 2][e & 3], &gf);
+              if constexpr (decltype(masked)::value)
+                y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
+              const float p = exp2_fast(y);
+              float ds;
+              if constexpr (DROP) {
+                const float4 n4 = nq[e >> 2];
+                const float nd =
+                    (e & 3) == 0 ? n4.x : (e & 3) == 1 ? n4.y : (e & 3) == 2 ? n4.z : n4.w;
+                ds = p * fmaf(keep_only(a.drop_scale, mw, r), pacc[r], nd);
+                sacc[r] = keep_only(p, mw, r);  // dV takes the kept weights; scaled at the end
+              } else {
+                ds = p * pacc[r];
+                sacc[r] = p;
+              }
+              if constexpr (MODE != kScoreScale) ds *= gf;
+              pacc[r] = ds;
+            }
+          };
+          if (need_mask)
+            grads(std::true_type{});
+          else
+            grads(std::false_type{});
+          const bf16x8 pb = pack8(sacc, 8 * t), dsb = pack8(pacc, 8 * t);
+          __builtin_amdgcn_sched_barrier(0);
+          bf16x8 ot[NDB], qt_[NDB];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int off = (qb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
+            ot[db] = tr_read_pair(so + off, so + off + 8 * LD);
+            qt_[db] = tr_read_pair(sq + off, sq + off + 8 * LD);
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dvacc[db] = mfma32(ot[db], pb, dvacc[db]);
+            dkacc[db] = mfma32(qt_[db], dsb, dkacc[db]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };

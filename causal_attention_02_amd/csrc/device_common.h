@@ -329,22 +329,46 @@ template <int D, int NW>
 struct TileDma {
   static constexpr int G = D / 8 + 1;
   static constexpr int NC = (G + NW - 1) / NW;  // chunks per wave (the last may be absent)
-  int rel[NC];                                  // granule offset from the tile start
+  uint32_t off[NC];  // byte offset of the chunk's source granule from the tile start
   __device__ __forceinline__ TileDma(int w, int l) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int pg = 64 * (w + NW * i) + l;
-      rel[i] = pg - pg / G;
+      off[i] = 16u * (uint32_t)(pg - pg / G);
     }
   }
-  // Copy rows r0.. of the head starting at src (T rows) into lds.
+  // Copy rows r0.. of the head starting at src (T rows) into lds (w: this wave's index).
   __device__ __forceinline__ void copy(bf16* lds, const bf16* src, int r0, int T, int w) const {
+    w = __builtin_amdgcn_readfirstlane(w);  // the LDS targets and chunk ownership are uniform
+    if (r0 + 64 < T) {
+      // Every source granule, the last row's pad included, lies inside the head: a uniform
+      // base plus the lane's 32-bit offset, which the hardware adds itself (no clamp and no
+      // per-lane 64-bit address arithmetic).
+      // The base is uniform; reading it from the first lane places it in scalar registers
+      // once per copy instead of once per load.
+      const uint64_t bv = reinterpret_cast<uint64_t>(src + (int64_t)r0 * D);
+      const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+      const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+      const char* base = reinterpret_cast<const char*>(((uint64_t)bhi << 32) | blo);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = w + NW * i;
+        if (c < G) {
+          // The empty asm keeps the offset a 32-bit value here (not a widened copy hoisted
+          // out of the loop), so the load takes the base-register-plus-offset form.
+          uint32_t o = off[i];
+          asm volatile("" : "+v"(o));
+          __builtin_amdgcn_global_load_lds(base + o, lds + 512 * c, 16, 0, 0);
+        }
+      }
+      return;
+    }
     const int first = r0 * (D / 8), last = T * (D / 8) - 1;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = w + NW * i;
       if (c < G) {
-        const bf16* from = src + 8 * (int64_t)min(first + rel[i], last);
+        const bf16* from = src + 8 * (int64_t)min(first + (int)(off[i] >> 4), last);
         __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
       }
     }
