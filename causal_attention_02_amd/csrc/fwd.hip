@@ -210,63 +210,81 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
       const int qd = off + qi - k0 - 4 * gl;
       if constexpr (FIXED) {
         // One straight-line body per mask variant, software-pipelined over the two 32-key
-        // blocks: block 1's score MFMAs are interleaved with block 0's weight VALU work, and
-        // block 0's PV MFMAs with block 1's (sched_group_barrier fixes the interleave).
+        // blocks in steps fenced by scheduling barriers: block 1's score MFMAs each followed
+        // by a share of block 0's weights, then block 0's PV MFMAs each followed by a share
+        // of block 1's weights.  LDS operands are read two steps ahead of their MFMA.
         auto body = [&](auto masked) {
           constexpr bool MASKED = decltype(masked)::value;
+          constexpr int KPF = 2, VPF = 2;  // steps an LDS operand read runs ahead of its MFMA
+          // Three waves per SIMD leave no register to spare: there the fences hold only the
+          // MFMA and memory instructions and let scalar and vector work cross (the weights are
+          // still held to their step by the asm pins), which lets the allocator fit.
+          constexpr int kFence = (D <= 96 && VAR == kVarPlain) ? 0x6 : 0;
           f32x16 sacc[2];
+          auto weight = [&](int kb, int r) {
+            float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
+            if constexpr (MASKED)
+              y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
+            sacc[kb][r] = exp2_fast(y);
+            // Pins the element's arithmetic to the step that asks for it.
+            asm volatile("" : "+v"(sacc[kb][r]));
+          };
+          // The block's weights rounded to bf16 in MFMA operand order; the row sum is taken
+          // over the rounded values, the ones the PV product uses, so the normalisation
+          // matches the numerator exactly (a single visible key returns V).
+          auto pack = [&](int kb, bf16x8 (&pb)[2]) {
+            pb[0] = pack8(sacc[kb], 0);
+            pb[1] = pack8(sacc[kb], 8);
+            l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
+            if constexpr (DROP) {
+              pb[0] = keep_packed(pb[0], mw[kb], 0);
+              pb[1] = keep_packed(pb[1], mw[kb], 1);
+            }
+          };
+          auto k_ptr = [&](int kb, int s) { return sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl; };
+          auto v_ptr = [&](int kb, int i) {  // PV step i = NDB t + db
+            return sv + (kb * 32 + 16 * (i / NDB) + trow) * LD + 32 * (i % NDB) + tcol;
+          };
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 ka[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-              ka[s] = ld16<bf16x8>(sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl);
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+          // Both blocks' score MFMAs as one stream of 2 NS steps (step j: block j / NS, slice
+          // j % NS); block 1's steps each carry a share of block 0's weights.
+          bf16x8 kr[KPF];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) sacc[kb] = mfma32(ka[s], bq[s], sacc[kb]);
+          for (int j = 0; j < KPF; ++j) kr[j] = ld16<bf16x8>(k_ptr(j / NS, j % NS));
+#pragma unroll
+          for (int j = 0; j < 2 * NS; ++j) {
+            const int kb = j / NS, s = j % NS;
+            sacc[kb] = mfma32(kr[j % KPF], bq[s], sacc[kb]);
+            if (j + KPF < 2 * NS)
+              kr[j % KPF] = ld16<bf16x8>(k_ptr((j + KPF) / NS, (j + KPF) % NS));
+            if (kb == 1) {
+#pragma unroll
+              for (int r = 16 * s / NS; r < 16 * (s + 1) / NS; ++r) weight(0, r);
+            }
+            __builtin_amdgcn_sched_barrier(kFence);
           }
           bf16x8 pb[2][2];
+          pack(0, pb[0]);
+          bf16x8 vr[VPF];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
-              if constexpr (MASKED)
-                y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
-              sacc[kb][r] = exp2_fast(y);
-            }
-            pb[kb][0] = pack8(sacc[kb], 0);
-            pb[kb][1] = pack8(sacc[kb], 8);
-            // Row sum of the bf16-rounded weights, the values the PV product uses, so the
-            // normalisation matches the numerator exactly (a single visible key returns V).
-            l_run += sum_bf16x8(pb[kb][0]) + sum_bf16x8(pb[kb][1]);
-            if constexpr (DROP) {
-              pb[kb][0] = keep_packed(pb[kb][0], mw[kb], 0);
-              pb[kb][1] = keep_packed(pb[kb][1], mw[kb], 1);
-            }
-            pv_block<D>(oacc, sv, kb, pb[kb], trow, tcol);
-          }
-          // Schedule: block 0 scores; block 1's K reads and score MFMAs under block 0's
-          // weights; block 0's PV under block 1's weights; block 1's PV.
-          // VALU ops per interleave slot (dropout adds 16 per packed half block).
-          constexpr int VW = (MASKED ? 26 : 22) + (DROP ? (32 + NS - 1) / NS : 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
-#pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, VW, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB, 0);
+          for (int i = 0; i < VPF; ++i) vr[i] = tr_read_pair(v_ptr(0, i), v_ptr(0, i) + 8 * LD);
+          __builtin_amdgcn_sched_barrier(kFence);
 #pragma unroll
           for (int i = 0; i < 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, VW * NS / (2 * NDB), 0);
+            oacc[i % NDB] = mfma32(vr[i % VPF], pb[0][i / NDB], oacc[i % NDB]);
+            if (i + VPF < 2 * NDB)
+              vr[i % VPF] = tr_read_pair(v_ptr(0, i + VPF), v_ptr(0, i + VPF) + 8 * LD);
+#pragma unroll
+            for (int r = 16 * i / (2 * NDB); r < 16 * (i + 1) / (2 * NDB); ++r) weight(1, r);
+            __builtin_amdgcn_sched_barrier(kFence);
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDB, 0);
+          pack(1, pb[1]);
+          // Block 1's PV, scheduled by the compiler.
+          pv_block<D>(oacc, sv, 1, pb[1], trow, tcol);
+          __builtin_amdgcn_sched_barrier(kFence);
         };
         if (need_mask)
           body(std::true_type{});
