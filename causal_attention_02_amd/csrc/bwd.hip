@@ -555,9 +555,10 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  // One q tile against this wave's 32 keys, operands in (sq, so, sl, sd), keep words in sm.
-  auto step = [&](int it, const bf16* sq, const bf16* so, const float* sl, const float* sd,
-                  const uint32_t* sm) {
+  // One q tile against this wave's 32 keys, operands in (sq, so, sl, sd), keep words in sm:
+  // the two 32-query blocks one after the other.
+  auto step_split = [&](int it, const bf16* sq, const bf16* so, const float* sl,
+                        const float* sd, const uint32_t* sm) __attribute__((always_inline)) {
     const int hh = it / nq;
     const int q0 = (qt0 + it - hh * nq) * kBMt;
     const int q_last = min(q0 + kBMt - 1, T - 1);
@@ -743,6 +744,144 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
         }
       }
     }
+  };
+
+  // The same q tile with the two query blocks overlapped, for one wave per SIMD (the wave
+  // has no partner to fill its idle units, and 512 registers hold both blocks' scores):
+  // block 0's S / dP products; block 1's products beside block 0's gradient; block 0's dV /
+  // dK products beside block 1's gradient; block 1's dV / dK products.  Steps are fenced by
+  // scheduling barriers, the gradient pinned to its step, LDS operands read two steps ahead.
+  auto step_full = [&](int it, const bf16* sq, const bf16* so, const float* sl,
+                       const float* sd, const uint32_t* sm) __attribute__((always_inline)) {
+    const int hh = it / nq;
+    const int q0 = (qt0 + it - hh * nq) * kBMt;
+    const int q_last = min(q0 + kBMt - 1, T - 1);
+    const bool skip = !wave_active || q_last < kw0 || q0 > e_hi ||
+                      (window > 0 && q0 > kw_last + window - 1);
+    if (skip) return;
+    const bool need_mask = (q0 < kw_last) || (q0 + kBMt > T) || q_last > e_lo ||
+                           (window > 0 && q_last - kw0 >= window);
+    // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
+    const int kd = q0 + 4 * gl - kj;
+    auto body = [&](auto masked) {
+      f32x16 sacc[2], pacc[2];
+      uint32_t mw[2] = {0u, 0u};
+      // Per block and element group j = r / 4: LSE and -D of queries 8 j + 4 gl .. + 3.
+      float4 lq[2][4], nq4[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lq[qb][j] = *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 8 * j);
+          nq4[qb][j] = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 8 * j);
+        }
+        if constexpr (DROP) mw[qb] = sm[qb * kBNkv + kj - kwg0] >> (4 * gl);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[qb][r] = 0.f;  // zero accumulators need no vector instructions before the MFMA
+          pacc[qb][r] = 0.f;
+        }
+      }
+      auto pick = [](const float4& v, int c) {
+        return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+      };
+      // Gradient of element r of block qb: P (dV operand) into sacc, dS into pacc.
+      auto grad = [&](int qb, int r) {
+        const int qo = 8 * (r >> 2) + (r & 3);
+        float gf;
+        float y = score_grad<MODE>(sacc[qb][r], a.sc, pick(lq[qb][r >> 2], r & 3), &gf);
+        if constexpr (decltype(masked)::value)
+          y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
+        const float p = exp2_fast(y);
+        const float nd = pick(nq4[qb][r >> 2], r & 3);
+        float ds;
+        if constexpr (DROP) {
+          ds = p * fmaf(keep_only(a.drop_scale, mw[qb], r), pacc[qb][r], nd);
+          sacc[qb][r] = keep_only(p, mw[qb], r);  // dV takes the kept weights; scaled at the end
+        } else {
+          ds = p * (pacc[qb][r] + nd);
+          sacc[qb][r] = p;
+        }
+        if constexpr (MODE != kScoreScale) ds *= gf;
+        pacc[qb][r] = ds;
+        asm volatile("" : "+v"(sacc[qb][r]), "+v"(pacc[qb][r]));
+      };
+      auto qk_off = [&](int qb, int s) { return (qb * 32 + lr) * LD + 16 * s + 8 * gl; };
+      auto tr_off = [&](int qb, int i) {  // product step i = NDB t + db
+        return (qb * 32 + 16 * (i / NDB) + trow) * LD + 32 * (i % NDB) + tcol;
+      };
+      // S / dP products of both blocks as one stream of 2 NS steps (step j: block j / NS,
+      // slice j % NS); block 1's steps each carry a share of block 0's gradient.
+      bf16x8 qa[2], oa[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        qa[j] = ld16<bf16x8>(sq + qk_off(j / NS, j % NS));
+        oa[j] = ld16<bf16x8>(so + qk_off(j / NS, j % NS));
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * NS; ++j) {
+        const int qb = j / NS, s = j % NS;
+        sacc[qb] = mfma32(qa[j & 1], bk[s], sacc[qb]);
+        pacc[qb] = mfma32(oa[j & 1], bv[s], pacc[qb]);
+        if (j + 2 < 2 * NS) {
+          qa[j & 1] = ld16<bf16x8>(sq + qk_off((j + 2) / NS, (j + 2) % NS));
+          oa[j & 1] = ld16<bf16x8>(so + qk_off((j + 2) / NS, (j + 2) % NS));
+        }
+        if (qb == 1) {
+#pragma unroll
+          for (int r = 16 * s / NS; r < 16 * (s + 1) / NS; ++r) grad(0, r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // dV^T += dO^T P and dK^T += q^T dS of both blocks as one stream of 4 NDB steps (step
+      // i: block i / (2 NDB), product i % (2 NDB)); block 0's steps carry block 1's gradient.
+      bf16x8 pb[2][2], dsb[2][2];
+      pb[0][0] = pack8(sacc[0], 0);
+      pb[0][1] = pack8(sacc[0], 8);
+      dsb[0][0] = pack8(pacc[0], 0);
+      dsb[0][1] = pack8(pacc[0], 8);
+      bf16x8 ot[2], qt_[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ot[i] = tr_read_pair(so + tr_off(0, i), so + tr_off(0, i) + 8 * LD);
+        qt_[i] = tr_read_pair(sq + tr_off(0, i), sq + tr_off(0, i) + 8 * LD);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4 * NDB; ++i) {
+        const int qb = i / (2 * NDB), k = i % (2 * NDB), db = k % NDB, t = k / NDB;
+        if (i == 2 * NDB) {
+          pb[1][0] = pack8(sacc[1], 0);
+          pb[1][1] = pack8(sacc[1], 8);
+          dsb[1][0] = pack8(pacc[1], 0);
+          dsb[1][1] = pack8(pacc[1], 8);
+        }
+        dvacc[db] = mfma32(ot[i & 1], pb[qb][t], dvacc[db]);
+        dkacc[db] = mfma32(qt_[i & 1], dsb[qb][t], dkacc[db]);
+        if (i + 2 < 4 * NDB) {
+          const int o = tr_off((i + 2) / (2 * NDB), (i + 2) % (2 * NDB));
+          ot[i & 1] = tr_read_pair(so + o, so + o + 8 * LD);
+          qt_[i & 1] = tr_read_pair(sq + o, sq + o + 8 * LD);
+        }
+        if (qb == 0) {
+#pragma unroll
+          for (int r = 16 * k / (2 * NDB); r < 16 * (k + 1) / (2 * NDB); ++r) grad(1, r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (need_mask)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  };
+
+  auto step = [&](int it, const bf16* sq, const bf16* so, const float* sl, const float* sd,
+                  const uint32_t* sm) __attribute__((always_inline)) {
+    if constexpr (D >= 128 || (DROP && D >= 96))
+      step_full(it, sq, so, sl, sd, sm);
+    else
+      step_split(it, sq, so, sl, sd, sm);
   };
 
   // Two-deep pipeline over the (query head, query tile) iterations, unrolled by two so each
