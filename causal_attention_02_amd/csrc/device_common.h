@@ -373,25 +373,60 @@ struct TileDma {
       }
     }
   }
-  // The same copy with the offsets recomputed in place (three VALU ops per chunk) instead of
-  // held in registers; the empty asm keeps the compiler from hoisting them out of the loop.
-  // LO: rows below `lo` (left padding of a cache) read row lo instead, so that whatever
-  // those rows hold (they are masked, but a NaN times a zero weight would still be NaN)
-  // never enters the tile.
-  template <bool LO = false>
-  static __device__ __forceinline__ void copy_fresh(bf16* lds, const bf16* src, int r0, int T,
-                                                    int w, int l, int lo = 0) {
-    asm volatile("" : "+v"(l));
+};
+
+// The same copies for a kernel with no register to spare: the per-lane byte offsets (each
+// below 2^16: at most 64 G granules of 16 bytes) are held two to a register and extracted
+// with one instruction per chunk.
+template <int D, int NW>
+struct TileDma16 {
+  static constexpr int G = D / 8 + 1;
+  static constexpr int NC = (G + NW - 1) / NW;
+  static_assert(64 * G * 16 <= 65536, "offsets must fit 16 bits");
+  uint32_t off2[(NC + 1) / 2];
+  __device__ __forceinline__ TileDma16(int w, int l) {
+#pragma unroll
+    for (int i = 0; i < (NC + 1) / 2; ++i) off2[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int pg = 64 * (w + NW * i) + l;
+      off2[i / 2] |= (16u * (uint32_t)(pg - pg / G)) << (16 * (i & 1));
+    }
+  }
+  __device__ __forceinline__ uint32_t off(int i) const {
+    uint32_t o = (i & 1) ? off2[i / 2] >> 16 : off2[i / 2] & 0xffffu;
+    asm volatile("" : "+v"(o));  // extracted here, not hoisted out of the loop
+    return o;
+  }
+  // Copy rows r0.. of the head starting at src (T rows) into lds.  Rows below `lo` (left
+  // padding of a cache) read row lo instead, so that whatever those rows hold (they are
+  // masked, but a NaN times a zero weight would still be NaN) never enters the tile.
+  __device__ __forceinline__ void copy(bf16* lds, const bf16* src, int r0, int T, int w,
+                                       int lo) const {
+    w = __builtin_amdgcn_readfirstlane(w);
+    if (r0 + 64 < T && r0 >= lo) {
+      // Every source granule lies inside the head: uniform base plus 32-bit lane offset.
+      const uint64_t bv = reinterpret_cast<uint64_t>(src + (int64_t)r0 * D);
+      const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+      const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+      const char* base = reinterpret_cast<const char*>(((uint64_t)bhi << 32) | blo);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = w + NW * i;
+        if (c < G) {
+          const uint32_t o = off(i);
+          __builtin_amdgcn_global_load_lds(base + o, lds + 512 * c, 16, 0, 0);
+        }
+      }
+      return;
+    }
     const int first = r0 * (D / 8), last = T * (D / 8) - 1, lo_g = lo * (D / 8);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = w + NW * i;
       if (c < G) {
-        const int pg = 64 * c + l;
-        int gsrc = min(first + pg - pg / G, last);
-        if constexpr (LO) gsrc = max(gsrc, lo_g);
-        const bf16* from = src + 8 * (int64_t)gsrc;
-        __builtin_amdgcn_global_load_lds(from, lds + 512 * c, 16, 0, 0);
+        const int gsrc = max(min(first + (int)(off(i) >> 4), last), lo_g);
+        __builtin_amdgcn_global_load_lds(src + 8 * (int64_t)gsrc, lds + 512 * c, 16, 0, 0);
       }
     }
   }

@@ -164,9 +164,10 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
 
   // Tile loads: rows past T read clamped, finite data whose scores the causal mask removes
   // (such keys lie after every query).
+  const TileDma16<D, 4> tdma(w, l);
   auto dma = [&](int kt, int buf) {
-    TileDma<D, 4>::template copy_fresh<PACKED>(buf ? sK1 : sK0, kbase, kt * kBN, nk, w, l, S0);
-    TileDma<D, 4>::template copy_fresh<PACKED>(buf ? sV1 : sV0, vbase, kt * kBN, nk, w, l, S0);
+    tdma.copy(buf ? sK1 : sK0, kbase, kt * kBN, nk, w, PACKED ? S0 : 0);
+    tdma.copy(buf ? sV1 : sV0, vbase, kt * kBN, nk, w, PACKED ? S0 : 0);
     if constexpr (DROP) {
       // Wave w: keep word of block (w & 1) for queries q0 + 64 (w >> 1) + lane.
       const int row = min(q0 + 64 * (w >> 1) + l, T - 1);
