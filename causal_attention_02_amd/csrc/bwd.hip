@@ -265,36 +265,30 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
           sacc[kb][r] = 0.f;  // zero accumulators need no vector instructions before the MFMA
           pacc[kb][r] = 0.f;
         }
-      // Block 0's products, scheduled by the compiler.
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 ka = ld16<bf16x8>(sk + kv_off(0, s));
-        const bf16x8 va = ld16<bf16x8>(sv + kv_off(0, s));
-        sacc[0] = mfma32(ka, bq[s], sacc[0]);
-        pacc[0] = mfma32(va, bdo[s], pacc[0]);
-      }
       // Operand reads run PF steps ahead of their MFMAs (one where dropout's keep words leave
       // no registers for a second set).
       constexpr int PF = (DROP && D >= 96) ? 1 : 2;
+      // Both blocks' S / dP products as one stream of 2 NS steps (step j: block j / NS, slice
+      // j % NS); block 1's steps each carry a share of block 0's dS.
       bf16x8 ka[PF], va[PF];
 #pragma unroll
-      for (int s = 0; s < PF; ++s) {
-        ka[s] = ld16<bf16x8>(sk + kv_off(1, s));
-        va[s] = ld16<bf16x8>(sv + kv_off(1, s));
+      for (int j = 0; j < PF; ++j) {
+        ka[j] = ld16<bf16x8>(sk + kv_off(j / NS, j % NS));
+        va[j] = ld16<bf16x8>(sv + kv_off(j / NS, j % NS));
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // Block 1's products, each pair followed by a later pair's operand reads and a share of
-      // block 0's dS.
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc[1] = mfma32(ka[s % PF], bq[s], sacc[1]);
-        pacc[1] = mfma32(va[s % PF], bdo[s], pacc[1]);
-        if (s + PF < NS) {
-          ka[s % PF] = ld16<bf16x8>(sk + kv_off(1, s + PF));
-          va[s % PF] = ld16<bf16x8>(sv + kv_off(1, s + PF));
+      for (int j = 0; j < 2 * NS; ++j) {
+        const int kb = j / NS, s = j % NS;
+        sacc[kb] = mfma32(ka[j % PF], bq[s], sacc[kb]);
+        pacc[kb] = mfma32(va[j % PF], bdo[s], pacc[kb]);
+        if (j + PF < 2 * NS) {
+          ka[j % PF] = ld16<bf16x8>(sk + kv_off((j + PF) / NS, (j + PF) % NS));
+          va[j % PF] = ld16<bf16x8>(sv + kv_off((j + PF) / NS, (j + PF) % NS));
         }
+        if (kb == 1) {
 #pragma unroll
-        for (int r = 16 * s / NS; r < 16 * (s + 1) / NS; ++r) grad(0, r);
+          for (int r = 16 * s / NS; r < 16 * (s + 1) / NS; ++r) grad(0, r);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       dsb[0][0] = pack8(sacc[0], 0);
