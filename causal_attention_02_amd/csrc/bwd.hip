@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
   const int T = a.T;
   const int nbh = a.B * a.Hq;
   const int rank = blockIdx.x / nbh;
-  const int bh = blockIdx.x - rank * nbh;
+  const int bh = xcd_local_head(blockIdx.x - rank * nbh, nbh);
   const int qt = a.ntiles - 1 - rank;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
@@ -293,34 +293,34 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
       }
       dsb[0][0] = pack8(sacc[0], 0);
       dsb[0][1] = pack8(sacc[0], 8);
+      // Both blocks' dQ products as one stream of 4 NDB steps (step i: block i / (2 NDB),
+      // product i % (2 NDB) = NDB t + db).  Block 1's dS shares them out by halves: elements
+      // 0-7 beside block 0's products, elements 8-15 beside block 1's first-half products,
+      // which need only elements 0-7.
+      auto kt_at = [&](int i) {
+        const bf16* p0 = kt_ptr(i / (2 * NDB), i % (2 * NDB));
+        return tr_read_pair(p0, p0 + 8 * LD);
+      };
       bf16x8 kt_[PF];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) kt_[i] = tr_read_pair(kt_ptr(0, i), kt_ptr(0, i) + 8 * LD);
+      for (int i = 0; i < PF; ++i) kt_[i] = kt_at(i);
       __builtin_amdgcn_sched_barrier(0);
-      // Block 0's dQ products, each followed by a later operand's reads and a share of
-      // block 1's dS.
 #pragma unroll
-      for (int i = 0; i < 2 * NDB; ++i) {
-        dqacc[i % NDB] = mfma32(kt_[i % PF], dsb[0][i / NDB], dqacc[i % NDB]);
-        if (i + PF < 2 * NDB)
-          kt_[i % PF] = tr_read_pair(kt_ptr(0, i + PF), kt_ptr(0, i + PF) + 8 * LD);
+      for (int i = 0; i < 4 * NDB; ++i) {
+        const int kb = i / (2 * NDB), k = i % (2 * NDB);
+        if (i == 2 * NDB) dsb[1][0] = pack8(sacc[1], 0);
+        if (i == 3 * NDB) dsb[1][1] = pack8(sacc[1], 8);
+        dqacc[k % NDB] = mfma32(kt_[i % PF], dsb[kb][k / NDB], dqacc[k % NDB]);
+        if (i + PF < 4 * NDB) kt_[i % PF] = kt_at(i + PF);
+        if (i < 3 * NDB) {
+          const int h = i / (2 * NDB) == 0 ? i : i - 2 * NDB;  // step within its share
+          const int n = i < 2 * NDB ? 2 * NDB : NDB;          // steps in the share
+          const int r0 = i < 2 * NDB ? 0 : 8;
 #pragma unroll
-        for (int r = 16 * i / (2 * NDB); r < 16 * (i + 1) / (2 * NDB); ++r) grad(1, r);
+          for (int r = r0 + 8 * h / n; r < r0 + 8 * (h + 1) / n; ++r) grad(1, r);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      dsb[1][0] = pack8(sacc[1], 0);
-      dsb[1][1] = pack8(sacc[1], 8);
-      // Block 1's dQ products.
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 kr[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          kr[db] = tr_read_pair(kt_ptr(1, NDB * t + db), kt_ptr(1, NDB * t + db) + 8 * LD);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(kr[db], dsb[1][t], dqacc[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     };
     if (need_mask)
       body(std::true_type{});

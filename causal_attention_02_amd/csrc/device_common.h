@@ -316,6 +316,16 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ---- workgroup order ---------------------------------------------------------------------
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by index.  Within one
+// rank of a (rank, head) grid, index i runs on XCD i % 8; this returns the head for index i
+// such that each XCD gets a contiguous range of nbh / 8 heads, i.e. whole GQA groups whose
+// query heads share one K/V stream, instead of every 8th head.  The rank order (heaviest
+// tiles first) is untouched.  Identity when nbh is not a multiple of 8.
+__device__ __forceinline__ int xcd_local_head(int i, int nbh) {
+  return (nbh & 7) ? i : (i & 7) * (nbh >> 3) + (i >> 3);
+}
+
 // ---- tile staging ------------------------------------------------------------------------
 // Direct global -> LDS copies of 64-row bf16 tiles into LDS rows of pitch D + 8 elements
 // (the pad keeps the row-per-lane MFMA operand reads free of bank conflicts).  The LDS image

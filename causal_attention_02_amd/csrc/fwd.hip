@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
   const int T = a.T;  // query rows per head
   const int nbh = a.B * a.Hq;
   const int rank = blockIdx.x / nbh;  // heaviest (last) query tiles first
-  const int bh = blockIdx.x - rank * nbh;
+  const int bh = xcd_local_head(blockIdx.x - rank * nbh, nbh);
   const int qt = a.nqt - 1 - rank;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
