@@ -740,6 +740,140 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
     }
   };
 
+  // The same q tile in quarters (block qb, half t) at two waves per SIMD and d = 96 (at
+  // d <= 64 the steps are too short for it to pay; measured slower), where registers hold
+  // only one block's scores plus a half block: block 0's S / dP products; block 0's first
+  // half gradient and its dV / dK products; block 1's S / dP products beside block 0's second
+  // half gradient; block 0's second-half products beside block 1's first-half gradient;
+  // block 1's first-half products beside its second-half gradient; block 1's second-half
+  // products.
+  auto step_quarters = [&](int it, const bf16* sq, const bf16* so, const float* sl,
+                           const float* sd, const uint32_t* sm) __attribute__((always_inline)) {
+    const int hh = it / nq;
+    const int q0 = (qt0 + it - hh * nq) * kBMt;
+    const int q_last = min(q0 + kBMt - 1, T - 1);
+    const bool skip = !wave_active || q_last < kw0 || q0 > e_hi ||
+                      (window > 0 && q0 > kw_last + window - 1);
+    if (skip) return;
+    const bool need_mask = (q0 < kw_last) || (q0 + kBMt > T) || q_last > e_lo ||
+                           (window > 0 && q_last - kw0 >= window);
+    // iq - kj for element (qb, r) is kd + 32 qb + 8 (r / 4) + r % 4.
+    const int kd = q0 + 4 * gl - kj;
+    auto body = [&](auto masked) {
+      f32x16 sacc[2], pacc[2];
+      uint32_t mw[2] = {0u, 0u};
+      auto pick = [](const float4& v, int c) {
+        return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+      };
+      // S accumulates from 0; dP from -D (dropout: from 0, -D joins in the gradient).
+      auto setup = [&](int qb) {
+        if constexpr (DROP) mw[qb] = sm[qb * kBNkv + kj - kwg0] >> (4 * gl);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 nd = *reinterpret_cast<const float4*>(sd + qb * 32 + 4 * gl + 8 * j);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            sacc[qb][4 * j + c] = 0.f;
+            pacc[qb][4 * j + c] = DROP ? 0.f : pick(nd, c);
+          }
+        }
+      };
+      // Gradient of element r of block qb: P (dV operand) into sacc, dS into pacc.
+      auto grad = [&](int qb, int r) {
+        const int qo = 8 * (r >> 2) + (r & 3);
+        const float lse = sl[qb * 32 + 4 * gl + 8 * (r >> 2) + (r & 3)];
+        float gf;
+        float y = score_grad<MODE>(sacc[qb][r], a.sc, lse, &gf);
+        if constexpr (decltype(masked)::value)
+          y = visible(kd + 32 * qb + qo, lim) ? y : kNegBig;
+        const float p = exp2_fast(y);
+        float ds;
+        if constexpr (DROP) {
+          const float nd = sd[qb * 32 + 4 * gl + 8 * (r >> 2) + (r & 3)];
+          ds = p * fmaf(keep_only(a.drop_scale, mw[qb], r), pacc[qb][r], nd);
+          sacc[qb][r] = keep_only(p, mw[qb], r);  // dV takes the kept weights; scaled at the end
+        } else {
+          ds = p * pacc[qb][r];
+          sacc[qb][r] = p;
+        }
+        if constexpr (MODE != kScoreScale) ds *= gf;
+        pacc[qb][r] = ds;
+        asm volatile("" : "+v"(sacc[qb][r]), "+v"(pacc[qb][r]));
+      };
+      auto qk_off = [&](int qb, int s) { return (qb * 32 + lr) * LD + 16 * s + 8 * gl; };
+      auto tr_off = [&](int qb, int t, int db) {
+        return (qb * 32 + 16 * t + trow) * LD + 32 * db + tcol;
+      };
+      bf16x8 pb[2][2], dsb[2][2];
+      auto pack = [&](int qb, int t) {
+        pb[qb][t] = pack8(sacc[qb], 8 * t);
+        dsb[qb][t] = pack8(pacc[qb], 8 * t);
+      };
+      // dV / dK products of quarter (qb, t), step db carrying gradient elements
+      // [g0 + 8 db / NDB, g0 + 8 (db + 1) / NDB) of block gq (none when gq < 0).
+      auto quarter = [&](int qb, int t, int gq, int g0) {
+        bf16x8 ot = tr_read_pair(so + tr_off(qb, t, 0), so + tr_off(qb, t, 0) + 8 * LD);
+        bf16x8 qt_ = tr_read_pair(sq + tr_off(qb, t, 0), sq + tr_off(qb, t, 0) + 8 * LD);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = mfma32(ot, pb[qb][t], dvacc[db]);
+          dkacc[db] = mfma32(qt_, dsb[qb][t], dkacc[db]);
+          if (db + 1 < NDB) {
+            ot = tr_read_pair(so + tr_off(qb, t, db + 1), so + tr_off(qb, t, db + 1) + 8 * LD);
+            qt_ = tr_read_pair(sq + tr_off(qb, t, db + 1), sq + tr_off(qb, t, db + 1) + 8 * LD);
+          }
+          if (gq >= 0) {
+#pragma unroll
+            for (int r = g0 + 8 * db / NDB; r < g0 + 8 * (db + 1) / NDB; ++r) grad(gq, r);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // Block 0's products, scheduled by the compiler.
+      setup(0);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 qa = ld16<bf16x8>(sq + qk_off(0, s));
+        const bf16x8 oa = ld16<bf16x8>(so + qk_off(0, s));
+        sacc[0] = mfma32(qa, bk[s], sacc[0]);
+        pacc[0] = mfma32(oa, bv[s], pacc[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) grad(0, r);
+      pack(0, 0);
+      quarter(0, 0, -1, 0);
+      // Block 1's products beside block 0's second-half gradient.
+      setup(1);
+      bf16x8 qa = ld16<bf16x8>(sq + qk_off(1, 0));
+      bf16x8 oa = ld16<bf16x8>(so + qk_off(1, 0));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc[1] = mfma32(qa, bk[s], sacc[1]);
+        pacc[1] = mfma32(oa, bv[s], pacc[1]);
+        if (s + 1 < NS) {
+          qa = ld16<bf16x8>(sq + qk_off(1, s + 1));
+          oa = ld16<bf16x8>(so + qk_off(1, s + 1));
+        }
+#pragma unroll
+        for (int r = 8 + 8 * s / NS; r < 8 + 8 * (s + 1) / NS; ++r) grad(0, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pack(0, 1);
+      quarter(0, 1, 1, 0);
+      pack(1, 0);
+      quarter(1, 0, 1, 8);
+      pack(1, 1);
+      quarter(1, 1, -1, 0);
+    };
+    if (need_mask)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  };
+
   // The same q tile with the two query blocks overlapped, for one wave per SIMD (the wave
   // has no partner to fill its idle units, and 512 registers hold both blocks' scores):
   // block 0's S / dP products; block 1's products beside block 0's gradient; block 0's dV /
@@ -874,6 +1008,8 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
                   const uint32_t* sm) __attribute__((always_inline)) {
     if constexpr (D >= 128 || (DROP && D >= 96))
       step_full(it, sq, so, sl, sd, sm);
+    else if constexpr (D == 96 && MODE != kScoreCapExp)
+      step_quarters(it, sq, so, sl, sd, sm);
     else
       step_split(it, sq, so, sl, sd, sm);
   };

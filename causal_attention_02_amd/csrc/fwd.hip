@@ -216,7 +216,8 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
         // of block 1's weights.  LDS operands are read two steps ahead of their MFMA.
         auto body = [&](auto masked) {
           constexpr bool MASKED = decltype(masked)::value;
-          constexpr int KPF = 2, VPF = 2;  // steps an LDS operand read runs ahead of its MFMA
+          // Steps an LDS operand read runs ahead of its MFMA (V: one at three waves per SIMD).
+          constexpr int KPF = 2, VPF = (D <= 96 && VAR == kVarPlain) ? 1 : 2;
           // Three waves per SIMD leave no register to spare: there the fences hold only the
           // MFMA and memory instructions and let scalar and vector work cross (the weights are
           // still held to their step by the asm pins), which lets the allocator fit.
@@ -230,17 +231,13 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
             // Pins the element's arithmetic to the step that asks for it.
             asm volatile("" : "+v"(sacc[kb][r]));
           };
-          // The block's weights rounded to bf16 in MFMA operand order; the row sum is taken
+          // Half t of a block's weights rounded to bf16 in MFMA operand order; the row sum is taken
           // over the rounded values, the ones the PV product uses, so the normalisation
           // matches the numerator exactly (a single visible key returns V).
-          auto pack = [&](int kb, bf16x8 (&pb)[2]) {
-            pb[0] = pack8(sacc[kb], 0);
-            pb[1] = pack8(sacc[kb], 8);
-            l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
-            if constexpr (DROP) {
-              pb[0] = keep_packed(pb[0], mw[kb], 0);
-              pb[1] = keep_packed(pb[1], mw[kb], 1);
-            }
+          auto pack = [&](int kb, int t, bf16x8& pb) {
+            pb = pack8(sacc[kb], 8 * t);
+            l_run += sum_bf16x8(pb);
+            if constexpr (DROP) pb = keep_packed(pb, mw[kb], t);
           };
           auto k_ptr = [&](int kb, int s) { return sk + (kb * 32 + lr) * LD + 16 * s + 8 * gl; };
           auto v_ptr = [&](int kb, int i) {  // PV step i = NDB t + db
@@ -267,25 +264,37 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
             }
             __builtin_amdgcn_sched_barrier(kFence);
           }
+          // Both blocks' PV MFMAs as one stream of 4 NDB steps (step i: block i / (2 NDB),
+          // product i % (2 NDB) = NDB t + db).  Block 1's weights share them out by halves:
+          // elements 0-7 beside block 0's products, 8-15 beside block 1's first-half
+          // products, which need only elements 0-7.
           bf16x8 pb[2][2];
-          pack(0, pb[0]);
+          pack(0, 0, pb[0][0]);
+          pack(0, 1, pb[0][1]);
+          auto v_at = [&](int i) {
+            const bf16* p0 = v_ptr(i / (2 * NDB), i % (2 * NDB));
+            return tr_read_pair(p0, p0 + 8 * LD);
+          };
           bf16x8 vr[VPF];
 #pragma unroll
-          for (int i = 0; i < VPF; ++i) vr[i] = tr_read_pair(v_ptr(0, i), v_ptr(0, i) + 8 * LD);
+          for (int i = 0; i < VPF; ++i) vr[i] = v_at(i);
           __builtin_amdgcn_sched_barrier(kFence);
 #pragma unroll
-          for (int i = 0; i < 2 * NDB; ++i) {
-            oacc[i % NDB] = mfma32(vr[i % VPF], pb[0][i / NDB], oacc[i % NDB]);
-            if (i + VPF < 2 * NDB)
-              vr[i % VPF] = tr_read_pair(v_ptr(0, i + VPF), v_ptr(0, i + VPF) + 8 * LD);
+          for (int i = 0; i < 4 * NDB; ++i) {
+            const int kb = i / (2 * NDB), k = i % (2 * NDB);
+            if (i == 2 * NDB) pack(1, 0, pb[1][0]);
+            if (i == 3 * NDB) pack(1, 1, pb[1][1]);
+            oacc[k % NDB] = mfma32(vr[i % VPF], pb[kb][k / NDB], oacc[k % NDB]);
+            if (i + VPF < 4 * NDB) vr[i % VPF] = v_at(i + VPF);
+            if (i < 3 * NDB) {
+              const int h = i < 2 * NDB ? i : i - 2 * NDB;  // step within its share
+              const int n = i < 2 * NDB ? 2 * NDB : NDB;    // steps in the share
+              const int r0 = i < 2 * NDB ? 0 : 8;
 #pragma unroll
-            for (int r = 16 * i / (2 * NDB); r < 16 * (i + 1) / (2 * NDB); ++r) weight(1, r);
+              for (int r = r0 + 8 * h / n; r < r0 + 8 * (h + 1) / n; ++r) weight(1, r);
+            }
             __builtin_amdgcn_sched_barrier(kFence);
           }
-          pack(1, pb[1]);
-          // Block 1's PV, scheduled by the compiler.
-          pv_block<D>(oacc, sv, 1, pb[1], trow, tcol);
-          __builtin_amdgcn_sched_barrier(kFence);
         };
         if (need_mask)
           body(std::true_type{});
