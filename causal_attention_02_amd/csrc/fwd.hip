@@ -69,6 +69,10 @@ __device__ __forceinline__ void pv_block(f32x16 (&oacc)[D / 32], const bf16* sv,
   }
 }
 
+// Largest factor (log2) a row's running maximum may grow by before the accumulators are
+// rescaled (running-maximum forward only).
+constexpr float kRescaleSlack = 8.f;
+
 // Kernel variants: plain rows; packed rows (segment ids); dropout on the weights.
 constexpr int kVarPlain = 0, kVarPacked = 1, kVarDrop = 2;
 
@@ -329,18 +333,25 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
         };
         float mx = need_mask ? scores(std::true_type{}) : scores(std::false_type{});
         mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+        // Lazy rescaling: the reference maximum moves (and the accumulators are rescaled) only
+        // when a row's maximum exceeds it by more than 2^8, decided for the whole wave; else
+        // the weights are taken against the old reference, at most 2^8.  Numerator and
+        // denominator share the reference, so the result is the same softmax.
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = exp2_fast(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(sacc[kb][r] - m_new);
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_fast(sacc[kb][r] - m_run);
           bf16x8 pb[2] = {pack8(sacc[kb], 0), pack8(sacc[kb], 8)};
           l_run += sum_bf16x8(pb[0]) + sum_bf16x8(pb[1]);
           if constexpr (DROP) {
