@@ -112,6 +112,9 @@ SMALL = [
     Workload("window1", B=1, T=70, Hq=2, Hkv=1, D=32, window=1, rope=True, qk_norm=True),
     Workload("window_gt_T", B=1, T=200, Hq=2, Hkv=2, D=64, window=205, qk_norm=True),
     Workload("mha_d64", B=2, T=256, Hq=4, Hkv=4, D=64, rope=True, softcap=20.0),
+    # soft-cap without QK-norm at d = 96: the exp-form score path, whose dK/dV keeps the
+    # phased half-block order at two waves per SIMD
+    Workload("cap_exp_d96", B=2, T=200, Hq=4, Hkv=2, D=96, softcap=30.0, rope=True),
 ]
 
 
@@ -129,16 +132,18 @@ def test_bf16_fwd_bwd_small(w):
     check_bf16(w, got, ref_f, ref_b, w.name, tol_grad=TOL_GRAD if w.T > 2 else 5e-2)
 
 
-def test_softcap_series_degree9():
-    """QK-norm with scale 0.19, D = 128 and cap 100 bounds |S / c| by 0.247: inside the
-    range of the degree-9 tanh series, but the degree-5 cut would move logits by ~4e-4,
-    more than its 2^-12 budget, so this takes the degree-9 score path in every kernel."""
+@pytest.mark.parametrize("D,scale", [(128, 0.19), (96, 0.25)])
+def test_softcap_series_degree9(D, scale):
+    """QK-norm bounds |S / c| by scale * D / c: 0.243 (D = 128, scale 0.19) and 0.24 (D = 96,
+    scale 0.25) with cap 100, inside the range of the degree-9 tanh series, where the
+    degree-5 cut would move logits by a few 1e-4, more than its 2^-12 budget; so these take
+    the degree-9 score path in every kernel."""
     import torch
-    w = Workload("poly9", B=1, T=200, Hq=2, Hkv=1, D=128, rope=True, qk_norm=True,
+    w = Workload("poly9", B=1, T=200, Hq=2, Hkv=1, D=D, rope=True, qk_norm=True,
                  softcap=100.0, seed=11)
-    opts = AttnOptions(softcap=100.0, scale=0.19, rope=True, qk_norm=True)
-    kw = dict(softcap=100.0, scale=0.19, rope=True, qk_norm=True)
-    _say(f"case {w.name}: D=128 scale=0.19 cap=100 norm")
+    opts = AttnOptions(softcap=100.0, scale=scale, rope=True, qk_norm=True)
+    kw = dict(softcap=100.0, scale=scale, rope=True, qk_norm=True)
+    _say(f"case {w.name}: D={D} scale={scale} cap=100 norm")
     q, k, v, dO = make_train_inputs(w)
     tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
     o, lse = attn_fwd(tq, tk, tv, opts)
