@@ -25,6 +25,10 @@
 //    come from ds_read_b64_tr_b16.  dK and dV of a KV head are summed over its query group
 //    inside the workgroup.
 //
+// Within a tile each wave issues one 32-row block's (or half block's) MFMAs beside another
+// block's gradient arithmetic, so its matrix and vector units work at once; how far that goes
+// depends on the registers the instantiation has (see the step and run variants).
+//
 // Dropout on the weights (O = (P * Z) V, Z = keep / (1 - rate)): dV = (P * Z)^T dO and
 // dS = P * (Z * (dO V^T) - D) with the same D.  The DROP instantiations stage each tile's
 // keep words in LDS beside it (row layout for dq, column layout for dkdv), start dP at 0

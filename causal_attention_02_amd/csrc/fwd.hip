@@ -18,6 +18,8 @@
 //     accumulators straight into the B operand of O^T += V^T P^T (no LDS round trip).
 //   * Key tiles wholly above the diagonal or outside the window are never visited; only
 //     tiles that straddle a mask edge evaluate the element mask.
+//   * Within a tile (two 32-key blocks) each wave issues one block's MFMAs beside the other
+//     block's weight arithmetic, so its matrix and vector units work at once.
 #include <type_traits>
 
 #include "device_common.h"
