@@ -517,11 +517,17 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
   const int nq = qt1 - qt0 + 1;
   const int nit = G * nq;
 
-  // Query tile of iteration it (query head hh = it / nq), from the diagonal down the sequence.
-  // (Walking from the last tile instead keeps a group's key blocks reading the same tiles at
-  // the same time and cut the fetches beyond L2 by a third at T = 2048, but was no faster and
-  // slower with short sequences or a window.)
-  auto q_tile = [&](int it, int hh) { return (qt0 + it - hh * nq) * kBMt; };
+  // Query tile of iteration it (query head hh = it / nq).  Without a window and with at least
+  // 8 tiles per head, from the last tile back to the diagonal: every key block of a KV group
+  // then starts at the same tile and walks in step with the others, so the workgroups on one
+  // XCD read each q^ / dO tile at about the same time and the L2 serves all but the first
+  // (a third fewer fetches beyond L2 at T = 2048, in the same time).  Otherwise from the
+  // diagonal down (the reversed walk was slower with a window or short ranges).
+  const bool walk_down = window == 0 && nq >= 8;
+  auto q_tile = [&](int it, int hh) {
+    const int u = it - hh * nq;
+    return (walk_down ? qt1 - u : qt0 + u) * kBMt;
+  };
   const TileDma<D, 4> tdma(w, l);
   // Issue the direct loads of iteration it's q^ / dO tiles and LSE / D vectors into
   // buffer `buf`; they are waited for at the end of the iteration that issues them.
