@@ -115,6 +115,9 @@ SMALL = [
     # soft-cap without QK-norm at d = 96: the exp-form score path, whose dK/dV keeps the
     # phased half-block order at two waves per SIMD
     Workload("cap_exp_d96", B=2, T=200, Hq=4, Hkv=2, D=96, softcap=30.0, rope=True),
+    # causal, no window, 10 query tiles of 64 for the first key block: dK/dV walks the tiles
+    # from the last one back there and from the diagonal down in the later key blocks
+    Workload("walk_t640", B=1, T=640, Hq=4, Hkv=2, D=96, softcap=50.0, rope=True, qk_norm=True),
 ]
 
 
