@@ -115,6 +115,10 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     stream = torch.cuda.current_stream()
+    dinfo = bd.device_info(0)
+    log(f"[bench] device: {dinfo['compute_units']} CUs at {dinfo['clock_khz'] / 1e3:.0f} MHz -> "
+        f"dense bf16 {dinfo['bf16_dense_tflops']:.0f} TFLOP/s; memory clock "
+        f"{dinfo['mem_clock_khz'] / 1e3:.0f} MHz x {dinfo['mem_bus_bits']} bits")
 
     def opts_of(w):
         return bd.AttnOptions(window=w.window, softcap=w.softcap, rope=w.rope,
@@ -243,6 +247,33 @@ def main():
                         frac=achieved / PEAK_BF16_TFLOPS, traffic=measured_traffic(dom),
                         algorithmic_flops_per_launch=algo_per_pair[fam] * pairs)
         result["roofline"] = roof
+        # MiniGPT shapes: the fp32 forward (B=2, T=128, 6 heads, d=32) and the bf16 training
+        # batch (B=32) -- both far too small to fill the GPU; reported per call.
+        w1 = WORKLOADS["minigpt_fwd_f32"]
+        q1, k1, v1, _ = make_train_inputs(w1)
+        t1 = [torch.from_numpy(x).to(dev).contiguous() for x in (q1, k1, v1)]
+        o1 = torch.empty_like(t1[0])
+        l1 = torch.empty(t1[0].shape[:3], dtype=torch.float32, device=dev)
+        opts1 = opts_of(w1)
+
+        def fwd32(_i=0):
+            bd.attn_fwd(t1[0], t1[1], t1[2], opts1, out=o1, lse=l1)
+
+        settle(fwd32, 0.2)
+        n1 = 200
+        us1 = timed(fwd32, n1) / n1 * 1e3
+        f1 = 4 * w1.D * visible_pairs(w1.T, w1.window) * w1.B * w1.Hq
+        extra["minigpt_fwd_f32"] = dict(us_per_call=us1, tflops=f1 / (us1 * 1e-6) / 1e12,
+                                        note="fp32 forward, 12 (b, h) units: launch-bound")
+        log(f"[bench] minigpt_fwd_f32: {us1:.1f} us/call")
+        w2 = WORKLOADS["minigpt_train_bf16"]
+        log(f"[bench] fwd+bwd {w2.name}")
+        ms2_, per2_, _ = train_case(w2, max(args.steps, 20), 5)
+        tf2_ = train_flops(w2) / (ms2_ * 1e-3) / 1e12
+        extra[w2.name] = dict(ms_per_step=ms2_, marker_ms_median=float(np.median(per2_)),
+                              tflops=tf2_, pct_peak=100 * tf2_ / PEAK_BF16_TFLOPS,
+                              note="192 (b, h) units of T=128: launch-bound")
+        log(f"[bench] {w2.name}: {ms2_ * 1e3:.1f} us/step  {tf2_:.1f} TFLOP/s")
         for name in ("flaxchat_full", "flaxchat_w512", "gpt_pretrain_train",
                      "gpt_pretrain_train_dropout", "gpt2xl_instruct_train"):
             w = WORKLOADS[name]
@@ -422,53 +453,87 @@ def main():
     # ------------------------------------------------------------------------------------
     cpu = None
     if not args.no_cpu_baseline and args.only in ("train", "all"):
-        from oracle import attention_backward, attention_forward
+        from oracle import attention_backward, attention_decode, attention_forward
+        try:
+            from threadpoolctl import threadpool_info, threadpool_limits
+            pools = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        except Exception:  # threadpoolctl missing: no BLAS metadata, no single-core leg
+            threadpool_limits, pools = None, []
+        threads = max([d.get("num_threads", 1) for d in pools] or [1])
+        blas = [{"library": d.get("internal_api"), "version": d.get("version"),
+                 "threads": d.get("num_threads")} for d in pools]
+
+        def okw(w):
+            return dict(window=w.window, softcap=w.softcap, rope=w.rope, rope_base=w.rope_base,
+                        qk_norm=w.qk_norm, norm_eps=w.norm_eps)
+
+        def run_for(seconds, fn):
+            """Call fn(i) for i = 0, 1, ... until `seconds` have passed; (calls, elapsed)."""
+            t0, n = time.perf_counter(), 0
+            while True:
+                fn(n)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return n, el
+
+        # The 181M workload: (batch, KV-group) slices, fwd + bwd.
         w = main_w
         q, k, v, dO = make_train_inputs(w)
         G = w.Hq // w.Hkv
-        kw = dict(window=w.window, softcap=w.softcap, rope=w.rope, rope_base=w.rope_base,
-                  qk_norm=w.qk_norm, norm_eps=w.norm_eps)
-        t0 = time.perf_counter()
-        units = 0
-        while True:
-            b, g = units % w.B, (units // w.B) % w.Hkv
+        kw = okw(w)
+
+        def slice_c3(i):
+            b, g = i % w.B, (i // w.B) % w.Hkv
             hs = slice(g * G, (g + 1) * G)
             attention_forward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], **kw)
             attention_backward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
                                dO[b:b + 1, hs], **kw)
-            units += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        el = time.perf_counter() - t0
-        sample_flops = train_flops(w.with_(B=1, Hq=G, Hkv=1)) * units
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-        except Exception:
-            threads = os.cpu_count()
-        cpu = {"value": sample_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+
+        units, el = run_for(args.cpu_seconds, slice_c3)
+        slice_flops = train_flops(w.with_(B=1, Hq=G, Hkv=1))
+        cpu = {"value": slice_flops * units / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
                "kind": "oracle",
                "sample": f"{units} (batch, KV-group) slices of {w.name} (1 x {G} query heads x "
-                         f"T={w.T} x d={w.D}) fwd+bwd in {el:.1f} s, host os.cpu_count()="
-                         f"{os.cpu_count()}"}
-        # The same oracle on one core, on a third of the time.
-        try:
-            from threadpoolctl import threadpool_limits
+                         f"T={w.T} x d={w.D}) fwd+bwd in {el:.1f} s",
+               "host": {"os_cpu_count": os.cpu_count(), "blas": blas,
+                        "threads_used": int(threads),
+                        "note": "numpy fp64; the BLAS pool's threads run the matrix products, "
+                                "the rest of the oracle is one Python thread"}}
+        if threadpool_limits is not None:
             with threadpool_limits(limits=1):
-                t0, n1 = time.perf_counter(), 0
-                while time.perf_counter() - t0 < args.cpu_seconds / 3:
-                    b, g = n1 % w.B, (n1 // w.B) % w.Hkv
-                    hs = slice(g * G, (g + 1) * G)
-                    attention_forward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], **kw)
-                    attention_backward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
-                                       dO[b:b + 1, hs], **kw)
-                    n1 += 1
-                el1 = time.perf_counter() - t0
-            cpu["single_core"] = {"value": train_flops(w.with_(B=1, Hq=G, Hkv=1)) * n1 / el1 / 1e12,
-                                  "unit": "TFLOP/s", "sample": f"{n1} slices in {el1:.1f} s"}
-        except Exception as e:  # threadpoolctl missing: report the multi-core figure only
-            cpu["single_core"] = {"error": str(e)}
+                n1, el1 = run_for(args.cpu_seconds / 3, slice_c3)
+            cpu["single_core"] = {"value": slice_flops * n1 / el1 / 1e12, "unit": "TFLOP/s",
+                                  "cores": 1, "sample": f"{n1} slices in {el1:.1f} s"}
         log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s over {units} slices")
+
+        # The other configurations, whole, beside their GPU lines (all host threads).
+        per = {}
+        w1 = WORKLOADS["minigpt_fwd_f32"]
+        a1 = make_train_inputs(w1)
+        n, el = run_for(1.0, lambda i: attention_forward(*a1[:3], **okw(w1)))
+        f1 = 4 * w1.D * visible_pairs(w1.T, w1.window) * w1.B * w1.Hq
+        per[w1.name] = {"us_per_call": el / n * 1e6, "TFLOP/s": f1 * n / el / 1e12,
+                        "sample": f"{n} whole forwards in {el:.1f} s"}
+        w2 = WORKLOADS["minigpt_train_bf16"]
+        a2 = make_train_inputs(w2)
+
+        def fb2(i):
+            attention_forward(*a2[:3], **okw(w2))
+            attention_backward(*a2, **okw(w2))
+
+        n, el = run_for(3.0, fb2)
+        per[w2.name] = {"ms_per_step": el / n * 1e3, "TFLOP/s": train_flops(w2) * n / el / 1e12,
+                        "sample": f"{n} whole fwd+bwd steps in {el:.1f} s"}
+        w5 = WORKLOADS["gqa181m_decode"]
+        qd5, kc5, vc5, lens5 = make_decode_inputs(w5)
+        dkw = {x: y for x, y in okw(w5).items() if x != "window"}
+        n, el = run_for(3.0, lambda i: attention_decode(qd5, kc5, vc5, lens5, **dkw))
+        per[w5.name] = {"us_per_call": el / n * 1e6,
+                        "GB/s": decode_bytes(w5, lens5) * n / el / 1e9,
+                        "sample": f"{n} whole decode calls (64 sequences) in {el:.1f} s"}
+        cpu["per_config"] = per
+        log(f"[bench] cpu oracle per config: {per}")
 
     line = {
         "metric": METRIC,
@@ -489,7 +554,13 @@ def main():
                    "global_batch": main_w.B, "seq_len": main_w.T, "parallelism": "single GPU"},
         "pct_of_peak": (100 * result["value"] / PEAK_BF16_TFLOPS
                         if args.only in ("train", "all") and result.get("value") else None),
-        "device": {"name": props.name, "cu": props.multi_processor_count},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "cu": dinfo["compute_units"], "clock_mhz": dinfo["clock_khz"] / 1e3,
+                   "bf16_dense_tflops_from_device": dinfo["bf16_dense_tflops"],
+                   "mem_clock_mhz": dinfo["mem_clock_khz"] / 1e3,
+                   "mem_bus_bits": dinfo["mem_bus_bits"]},
+        "peaks_used": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                       "source": "MI355X published dense figures"},
         "roofline": result.get("roofline"),
         "cpu_baseline": cpu,
         "extra": extra,

@@ -8,6 +8,7 @@ If the library is missing, every entry point raises -- there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -24,7 +25,7 @@ EXPORTED = [
     "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
     "attn_trace_enable", "attn_trace_read", "attn_dropout_mask_bytes", "attn_dropout_mask",
     "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_leftpad", "attn_extend_leftpad",
-    "attn_bwd_khat",
+    "attn_bwd_khat", "attn_device_info",
 ]
 
 
@@ -55,6 +56,12 @@ class AttnExtendCfg(ctypes.Structure):
 class AttnTraceEntry(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double)]
+
+
+class AttnDeviceInfo(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
+                ("mem_clock_khz", ctypes.c_int32), ("mem_bus_bits", ctypes.c_int32),
+                ("bf16_dense_tflops", ctypes.c_double)]
 
 
 class AttnError(RuntimeError):
@@ -123,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.attn_extend_leftpad.restype = ctypes.c_int
         L.attn_status_str.argtypes = [ctypes.c_int]
         L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_device_info.argtypes = [ctypes.c_int, ctypes.POINTER(AttnDeviceInfo)]
+        L.attn_device_info.restype = ctypes.c_int
         L.attn_trace_enable.argtypes = [ctypes.c_int]
         L.attn_trace_enable.restype = ctypes.c_int
         L.attn_trace_read.argtypes = [ctypes.POINTER(AttnTraceEntry), ctypes.c_int]
@@ -188,6 +197,20 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with `stream` (when given) as torch's current stream, so that the outputs
+    and the workspace it allocates belong to the stream the kernels are enqueued on.  The
+    caching allocator then reuses a freed workspace block only in that stream's order, after
+    the kernels that read it.  Buffers the caller passes in stay the caller's to order."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with _torch().cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 def _dtype_code(t):
     torch = _torch()
     if t.dtype == torch.bfloat16:
@@ -234,6 +257,7 @@ def dropout_mask_bytes(B, T, Hq, Hkv, D, opts: AttnOptions | None = None) -> int
     return int(lib().attn_dropout_mask_bytes(ctypes.byref(cfg)))
 
 
+@_on_stream
 def attn_dropout_mask(q, k, p: float, seed: int, offset: int = 0, opts: AttnOptions | None = None,
                       *, out=None, stream=None):
     """Keep mask (uint8 buffer of dropout_mask_bytes) for dropout rate p on the attention weights
@@ -254,6 +278,7 @@ def attn_dropout_mask(q, k, p: float, seed: int, offset: int = 0, opts: AttnOpti
     return m
 
 
+@_on_stream
 def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, workspace=None,
              stream=None, segment_ids=None, dropout_p=0.0, dropout_mask=None):
     """Forward: q [B,Hq,T,D], k/v [B,Hkv,T,D] (bf16 or fp32) -> (o, lse fp32 [B,Hq,T]).
@@ -304,6 +329,7 @@ def attn_fwd(q, k, v, opts: AttnOptions | None = None, *, out=None, lse=None, wo
     return o, lse_t
 
 
+@_on_stream
 def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, dk=None, dv=None,
              workspace=None, stream=None, segment_ids=None, dropout_p=0.0, dropout_mask=None,
              khat=None):
@@ -371,6 +397,7 @@ def attn_bwd(q, k, v, o, dO, lse, opts: AttnOptions | None = None, *, dq=None, d
     return dq, dk, dv
 
 
+@_on_stream
 def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None, *, split_len=0,
                 out=None, workspace=None, stream=None, cache_start=None):
     """Decode (bf16): q [B,Hq,D], caches [B,Hkv,Lmax,D], cache_len int32 [B] -> o [B,Hq,D].
@@ -405,6 +432,7 @@ def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None,
     return o
 
 
+@_on_stream
 def attn_extend(q, k_new, v_new, k_cache, v_cache, cache_len, opts: AttnOptions | None = None, *,
                 out=None, stream=None, cache_start=None):
     """S new tokens against a KV cache (bf16): q [B,Hq,S,D], k_new/v_new [B,Hkv,S,D], caches
@@ -435,6 +463,13 @@ def attn_extend(q, k_new, v_new, k_cache, v_cache, cache_len, opts: AttnOptions 
                            _ptr(v_cache), _ptr(cache_len), _ptr(o), _stream(stream))
     _check(st, "attn_extend")
     return o
+
+
+def device_info(device: int = 0) -> dict:
+    """Compute units, clocks, memory bus width and the dense bf16 MFMA peak of a HIP device."""
+    info = AttnDeviceInfo()
+    _check(lib().attn_device_info(int(device), ctypes.byref(info)), "attn_device_info")
+    return {f: getattr(info, f) for f, _ in AttnDeviceInfo._fields_}
 
 
 def trace_enable(on: bool = True):

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -22,13 +23,16 @@ struct TraceRec {
 };
 struct Tracer {
   std::mutex mu;
-  bool on = false;
+  bool on = false;  // guarded by mu
   std::vector<TraceRec> recs;
 };
 Tracer& tracer() {
   static Tracer t;
   return t;
 }
+// Read without a lock by every launch: while tracing is off (the default) a launch performs
+// this one relaxed load and touches no other shared state.
+std::atomic<bool> g_trace_on{false};
 void trace_clear_locked(Tracer& t) {
   for (auto& r : t.recs) {
     (void)hipEventDestroy(r.start);
@@ -39,6 +43,7 @@ void trace_clear_locked(Tracer& t) {
 }  // namespace
 
 TraceScope::TraceScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (!g_trace_on.load(std::memory_order_relaxed)) return;
   Tracer& t = tracer();
   std::lock_guard<std::mutex> lk(t.mu);
   if (!t.on) return;
@@ -488,11 +493,28 @@ int attn_extend_leftpad(const attn_extend_cfg* c, const void* q, const void* k_n
   return extend_impl(c, q, k_new, v_new, k_cache, v_cache, cache_start, cache_len, o, stream);
 }
 
+int attn_device_info(int device, attn_device_info_t* out) {
+  if (!out) return ATTN_EINVAL;
+  int cu = 0, clk = 0, mclk = 0, bus = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, device) != hipSuccess ||
+      hipDeviceGetAttribute(&mclk, hipDeviceAttributeMemoryClockRate, device) != hipSuccess ||
+      hipDeviceGetAttribute(&bus, hipDeviceAttributeMemoryBusWidth, device) != hipSuccess)
+    return ATTN_ELAUNCH;
+  out->compute_units = cu;
+  out->clock_khz = clk;
+  out->mem_clock_khz = mclk;
+  out->mem_bus_bits = bus;
+  out->bf16_dense_tflops = (double)cu * 4096.0 * clk * 1e3 / 1e12;
+  return ATTN_OK;
+}
+
 int attn_trace_enable(int on) {
   Tracer& t = tracer();
   std::lock_guard<std::mutex> lk(t.mu);
   if (on) trace_clear_locked(t);
   t.on = on != 0;
+  g_trace_on.store(t.on, std::memory_order_relaxed);
   return ATTN_OK;
 }
 

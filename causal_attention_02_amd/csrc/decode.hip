@@ -1,8 +1,8 @@
 // Single-token KV-cache decode on gfx950 ("GPT pretraining" page, section "Bonus: KV
-// Caching": the new token's key and value are appended to the cache and its one query
-// attends over the entire cached history; with offset = k_len - q_len = L - 1 every cached
-// key is visible).  The nanoGPT-JAX 181M model card's inference notes ask that only the
-// compact active part of the cache be attended; rows at or past cache_len[b] are never read.
+// Caching"): the cache of sequence b holds L = cache_len[b] rows, the newest token's key and
+// value among them, and that token's query sits at position L - 1, so no cached row is in its
+// future and all L are scored.  The nanoGPT-JAX 181M model card's inference notes ask that only
+// the compact active part of the cache be attended; rows at or past L are never read.
 // With left-padded batches (the same notes: left-padded prompts, right-aligned generation)
 // rows below cache_start[b] are padding and are not read either; positions count from there.
 //

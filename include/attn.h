@@ -17,17 +17,19 @@
  * _split_heads produces.  R is RoPE (pairs (x_i, x_{i+D/2}) rotated by p * base^(-2i/D)),
  * N the parameter-free RMSNorm x / sqrt(mean(x^2) + eps) -- both named on the nanoGPT-JAX
  * 181M model card ("Design choices worth naming") and on the flaxchat page ("Core
- * Features"), which also names the sliding window.  The KV-cache decode follows the
- * "Bonus: KV Caching" section of the GPT pretraining page: the new token's key/value are
- * already in the cache and its single query attends over the whole cached history;
- * attn_extend performs that section's whole step (append, then attend) for S new tokens.
+ * Features"), which also names the sliding window.  The KV-cache decode is the step of the
+ * "Bonus: KV Caching" section of the GPT pretraining page: the newest token's key and value
+ * are already stored at row L - 1 of its cache, and its query (position L - 1) is scored
+ * against rows 0 .. L - 1; attn_extend is the same step for S new tokens, including storing
+ * their keys and values.
  *
  * Conventions for every entry point below.
  *  - Pointers marked "device" are device memory owned by the caller; the library never
  *    allocates, frees or keeps them.  Tensors are dense and row-major in the stated shape.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  No call
- *    synchronises the host.  Calls share no mutable state and may run concurrently on
- *    different streams with different buffers.
+ *    synchronises the host.  Calls keep no state between them and may run concurrently on
+ *    different streams with different buffers: with the kernel trace off (the default), a
+ *    call reads one process-wide flag and writes no shared host or device state.
  *  - Argument errors are reported by a negative status BEFORE anything is enqueued.
  *    A failed launch is reported as ATTN_ELAUNCH.  Faults inside kernels surface at the
  *    caller's next synchronisation.
@@ -220,12 +222,12 @@ int attn_decode(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
                 size_t ws_bytes, void* stream);
 
 /*
- * attn_extend -- S new tokens per sequence against its KV cache.  The "Bonus: KV Caching"
- * section of the GPT pretraining page describes the step: compute the new tokens' keys and
- * values, append them to the cache, and let the new queries attend over the whole cached
- * history, query i seeing key j iff j <= offset + i with offset = the cached length.  With
- * cache_len = 0 this is the causal forward of the S tokens (prefill); with S = 1 it is
- * decode with the append done here.  bfloat16 only; no workspace.
+ * attn_extend -- S new tokens per sequence against its KV cache (the multi-token form of the
+ * step in the "Bonus: KV Caching" section of the GPT pretraining page).  New token i of
+ * sequence b sits at position p = cache_len[b] + i: its key and value are stored at cache row
+ * p, and its query is scored against cache rows j <= p.  With cache_len = 0 this is the
+ * causal forward of the S tokens (prefill); with S = 1 it is attn_decode plus the store.
+ * bfloat16 only; no workspace.
  *   q         [B, Hq, S, D] device, bf16 -- raw queries of the new tokens
  *   k_new, v_new [B, Hkv, S, D] device, bf16 -- raw keys and values of the new tokens
  *   k_cache, v_cache [B, Hkv, Lmax, D] device, bf16 -- rows < cache_len[b] hold the earlier
@@ -270,11 +272,29 @@ int attn_extend_leftpad(const attn_extend_cfg* cfg, const void* q, const void* k
 const char* attn_status_str(int status);
 
 /*
+ * attn_device_info -- host-only query of the figures a roofline needs, for HIP device
+ * `device` (no allocation, nothing enqueued).  bf16_dense_tflops = compute_units * clock *
+ * 4096 flops: gfx950's dense bf16 MFMA rate is 2048 multiply-adds per clock per compute unit.
+ * The memory clock and bus width are reported as the runtime gives them.  Returns ATTN_OK,
+ * ATTN_EINVAL for a null `out`, or ATTN_ELAUNCH if the runtime query fails.
+ */
+typedef struct {
+  int32_t compute_units;
+  int32_t clock_khz;       /* peak engine clock */
+  int32_t mem_clock_khz;   /* peak memory clock */
+  int32_t mem_bus_bits;    /* memory bus width */
+  double bf16_dense_tflops;
+} attn_device_info_t;
+
+int attn_device_info(int device, attn_device_info_t* out);
+
+/*
  * Kernel tracing (a measurement aid, off by default).  While enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events on its stream; attn_trace_read
  * synchronises those events and reports, per kernel name, the number of launches and
- * their summed device time.  The trace is process-wide state: enable/read/disable from
- * one thread while no other thread calls the library.
+ * their summed device time.  The trace is the library's only process-wide state (a flag,
+ * plus a mutex-guarded event list that only enabled tracing touches): enable/read/disable
+ * from one thread while no other thread calls the library.
  */
 typedef struct {
   char name[48];       /* kernel family, e.g. "fwd_bf16_d128"                                   */

@@ -21,11 +21,12 @@ What it computes (sources, by page title and section):
   model card, section "Architecture" (table and "Design choices worth naming");
   the same features and the sliding window are named on the flaxchat page, section
   "Core Features".
-* KV-cache decode: one new query attends over every cached key; with
-  offset = k_len - q_len, query i may see key j iff j <= offset + i -- "GPT
-  pretraining" page, section "Bonus: KV Caching".  The same section's step (compute
-  the new tokens' keys and values, append them to the cache, attend over the whole
-  history) with more than one new token is ``attention_extend``.
+* KV-cache decode -- "GPT pretraining" page, section "Bonus: KV Caching": the causal rule
+  measured from the cached length, i.e. new query i sits at position (rows cached
+  before the step) + i and may see cache row j iff j is not after that position; with
+  one new query whose key is already stored, every cached row is visible.  The same
+  step with several new tokens, storing their keys and values first, is
+  ``attention_extend``.
 
 Readings of what the pages leave open (each also listed with its reason in the
 project's design notes):
@@ -314,7 +315,7 @@ def attention_forward(q, k, v, *, window=0, softcap=0.0, scale=None, rope=False,
 
 def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=False,
                        rope_base=10000.0, qk_norm=False, norm_eps=1e-6, segment_ids=None,
-                       dropout_p=0.0, dropout_keep=None):
+                       dropout_p=0.0, dropout_keep=None, o_stored=None):
     """Analytic gradients (dQ, dK, dV) of <O, dO> with respect to the RAW q, k, v.
 
     Per (b, h) with g = kv head of h:
@@ -324,6 +325,8 @@ def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=F
       dS_pre = dS * (1 - tanh(S_pre / c)^2) if capped;
       dq^ = scale dS_pre k^;  dk^_g += scale dS_pre^T q^;
     then each of dq^, dk^ goes back through RMSNorm and RoPE.
+    o_stored [B, Hq, T, d] (optional): the output from which D is formed, e.g. the forward's
+    output as it is stored (rounded to bf16); by default the exact O.  Only D changes.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -355,7 +358,8 @@ def attention_backward(q, k, v, dO, *, window=0, softcap=0.0, scale=None, rope=F
             dP = dO[b, h] @ v[b, g].T
             if Z is not None:
                 dP = dP * Z
-            D = np.sum(dO[b, h] * O, axis=-1, keepdims=True)
+            Od = O if o_stored is None else np.asarray(o_stored, dtype=np.float64)[b, h]
+            D = np.sum(dO[b, h] * Od, axis=-1, keepdims=True)
             dS = P * (dP - D)
             if softcap > 0:
                 dS = dS * (1.0 - np.tanh(s_pre / softcap) ** 2)

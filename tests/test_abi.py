@@ -255,3 +255,8 @@ def test_status_strings_and_trace(L):
     bd.trace_enable(True)
     assert bd.trace_read() == {}
     bd.trace_enable(False)
+
+
+def test_device_info_rejects_null(L):
+    """Host-only: a null output is rejected before the runtime is asked anything."""
+    assert L.attn_device_info(0, None) == bd.ATTN_EINVAL

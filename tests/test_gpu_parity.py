@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on seeded inputs.
 
-Small cases compare every element; the full-size workloads (the shapes bench.py times, in
-the same launch configuration) compare sampled (batch, KV-group) slices, each of which the
-oracle computes exactly.  Tolerances: fp32 forward max-abs 1e-5; bf16 relative L2 1e-2
+Small cases compare every element; the full-size training workloads (the shapes bench.py
+times, in the same launch configuration) compare every (batch, KV-group) slice, each of which
+the oracle computes on its own.  Tolerances: fp32 forward max-abs 1e-5; bf16 relative L2 1e-2
 on O and 2e-2 on dQ/dK/dV; LSE absolute 2e-2 (bf16 inputs).
 """
 import sys
@@ -128,11 +128,15 @@ def test_bf16_fwd_bwd_small(w):
     q, k, v, dO = make_train_inputs(w)
     got = gpu_fwd_bwd(w, q, k, v, dO)
     ref_f = attention_forward(q, k, v, **oracle_kw(w))
-    ref_b = attention_backward(q, k, v, dO, **oracle_kw(w))
-    # With T <= 2 the first row of dQ (and the last row of dK) is exactly zero; there the
-    # backward leaves the residue of D_i = dO_i . O_i taken from the bf16-rounded O, about
-    # 2^-9 |dO_i| |O_i| / sqrt(D) -- a few percent of these tiny tensors' norms.
-    check_bf16(w, got, ref_f, ref_b, w.name, tol_grad=TOL_GRAD if w.T > 2 else 5e-2)
+    if w.T > 2:
+        ref_b = attention_backward(q, k, v, dO, **oracle_kw(w))
+    else:
+        # With T <= 2 the gradients are as small as the change that storing O in bf16 makes to
+        # D_i = dO_i . O_i (one rounding of O, relative 2^-9; measured 1.7 % of dQ/dK here).
+        # The backward forms D from the stored output, so the oracle does too.
+        ref_b = attention_backward(q, k, v, dO, o_stored=round_to_bf16(ref_f[0].astype(np.float32)),
+                                   **oracle_kw(w))
+    check_bf16(w, got, ref_f, ref_b, w.name)
 
 
 @pytest.mark.parametrize("D,scale", [(128, 0.19), (96, 0.25)])
@@ -169,27 +173,47 @@ def test_window_one_identity_on_gpu():
 
 
 # --------------------------------------------------------------------------------------------
-# Full-size workloads, sampled (b, kv-group) slices
+# Full-size workloads: every (b, kv-group) slice against the oracle
 # --------------------------------------------------------------------------------------------
 FULL = ["gqa181m_train", "flaxchat_full", "flaxchat_w512", "gpt_pretrain_train",
         "gpt2xl_instruct_train"]
 
 
+def check_every_slice(w, q, k, v, dO, got, name, okw):
+    """Each (b, KV group) slice -- the group's query heads with their KV head -- is computed by
+    the oracle on its own and compared with its own relative-L2 bounds."""
+    G = w.Hq // w.Hkv
+    worst = [0.0, 0.0]
+    n = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
+            kw = okw(b)
+            ref_f = attention_forward(qs, ks, vs, **kw)
+            ref_b = attention_backward(qs, ks, vs, dos, **kw)
+            sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
+                  got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
+            O_, L_ = sl[0], sl[1]
+            assert np.isfinite(O_).all() and np.isfinite(L_).all(), (name, b, g)
+            eO, eL = rel_l2(O_, ref_f[0]), max_abs(L_, ref_f[1])
+            eg = max(rel_l2(x, r) for x, r in zip(sl[2:], ref_b))
+            assert all(np.isfinite(x).all() for x in sl[2:]), (name, b, g)
+            assert eO <= TOL_O and eL <= TOL_LSE_BF16 and eg <= TOL_GRAD, (name, b, g, eO, eL, eg)
+            worst = [max(worst[0], eO), max(worst[1], eg)]
+            n += 1
+            if n % 16 == 0:
+                _say(f"  {name}: {n} slices checked, worst relL2 O {worst[0]:.2e} grads {worst[1]:.2e}")
+    _say(f"{name}: all {n} slices, worst relL2 O {worst[0]:.2e} grads {worst[1]:.2e}")
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size_every_slice(name):
     w = WORKLOADS[name]
     _say(f"case {name} full size: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
     q, k, v, dO = make_train_inputs(w)
     got = gpu_fwd_bwd(w, q, k, v, dO)
-    G = w.Hq // w.Hkv
-    for b, g in [(0, 0), (w.B // 2, w.Hkv // 2), (w.B - 1, w.Hkv - 1)]:
-        hs = slice(g * G, (g + 1) * G)
-        qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
-        ref_f = attention_forward(qs, ks, vs, **oracle_kw(w))
-        ref_b = attention_backward(qs, ks, vs, dos, **oracle_kw(w))
-        sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
-              got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
-        check_bf16(w, sl, ref_f, ref_b, f"{name}[b={b},g={g}]")
+    check_every_slice(w, q, k, v, dO, got, name, lambda b: oracle_kw(w))
 
 
 def test_bwd_khat_equals_bwd():
@@ -347,22 +371,14 @@ def test_packed_rows(case):
     check_bf16(w, got, attention_forward(q, k, v, **kw), attention_backward(q, k, v, dO, **kw), w.name)
 
 
-def test_packed_full_size_sampled():
+def test_packed_full_size_every_slice():
     w = WORKLOADS["gqa181m_sft_packed"]
     ids = make_segment_ids(w)
     _say(f"case {w.name} full size: B={w.B} T={w.T} runs of {w.seg_lo}..{w.seg_hi}")
     q, k, v, dO = make_train_inputs(w)
     got = gpu_fwd_bwd_packed(w, q, k, v, dO, ids)
-    G = w.Hq // w.Hkv
-    for b, g in [(0, 0), (w.B // 2, w.Hkv // 2), (w.B - 1, w.Hkv - 1)]:
-        hs = slice(g * G, (g + 1) * G)
-        qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], dO[b:b + 1, hs]
-        kw = dict(oracle_kw(w), segment_ids=ids[b:b + 1])
-        ref_f = attention_forward(qs, ks, vs, **kw)
-        ref_b = attention_backward(qs, ks, vs, dos, **kw)
-        sl = (got[0][b:b + 1, hs], got[1][b:b + 1, hs], got[2][b:b + 1, hs],
-              got[3][b:b + 1, g:g + 1], got[4][b:b + 1, g:g + 1])
-        check_bf16(w, sl, ref_f, ref_b, f"{w.name}[b={b},g={g}]")
+    check_every_slice(w, q, k, v, dO, got, w.name,
+                      lambda b: dict(oracle_kw(w), segment_ids=ids[b:b + 1]))
 
 
 # --------------------------------------------------------------------------------------------
@@ -807,6 +823,37 @@ def test_graph_replay_matches_eager():
         for i, (a, b) in enumerate(zip(outs, ref)):
             assert torch.equal(a, b), (rep, i)
     _say("graph replays match the eager step")
+
+
+def test_explicit_stream_argument():
+    """stream= given explicitly (not through torch's current stream): the wrappers allocate the
+    outputs and workspace on that stream, and the results equal those on the default stream
+    bitwise, also when other work is queued on the default stream meanwhile."""
+    import torch
+    w = WORKLOADS["gqa181m_train"].with_(B=2, T=400)
+    q, k, v, dO = make_train_inputs(w)
+    tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
+    opts = opts_of(w)
+    o, lse = attn_fwd(tq, tk, tv, opts)
+    ref = (o, lse) + attn_bwd(tq, tk, tv, o, tdo, lse, opts)
+    wd = WORKLOADS["gqa181m_decode"].with_(B=6, T=900)
+    qd, kc, vc, lens = make_decode_inputs(wd)
+    tqd, tkc, tvc = (to_dev(x, torch.bfloat16) for x in (qd, kc, vc))
+    tl = torch.from_numpy(lens).to("cuda")
+    refd = attn_decode(tqd, tkc, tvc, tl, opts_of(wd))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(rep)  # default-stream work that may reuse freed blocks
+        o2, lse2 = attn_fwd(tq, tk, tv, opts, stream=side)
+        g2 = attn_bwd(tq, tk, tv, o2, tdo, lse2, opts, stream=side)
+        od = attn_decode(tqd, tkc, tvc, tl, opts_of(wd), stream=side)
+        del junk
+        side.synchronize()
+        for a, b in zip((o2, lse2) + g2, ref):
+            assert torch.equal(a, b), rep
+        assert torch.equal(od, refd), rep
 
 
 def test_errors_on_gpu():

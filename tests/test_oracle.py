@@ -172,6 +172,44 @@ def test_gradient_sum_identities(flags):
         assert np.abs((k * dK).sum(-1)).max() < 1e-4
 
 
+def test_stored_output_enters_only_through_d():
+    """o_stored replaces the exact O in D_i = dO_i . O_i only.  Plain attention, closed form: a
+    change dD_i of D changes dS_ij by -P_ij dD_i, so dQ_i by -scale dD_i sum_j P_ij k_j and dK_j
+    by -scale sum_i P_ij dD_i q_i, and leaves dV.  With every flag set the change is still
+    linear in dD (twice the perturbation, twice the change) and dV is untouched."""
+    rng = np.random.default_rng(31)
+    B, H, T, d = 1, 2, 7, 6
+    q, k, v, dO = rnd(rng, B, H, T, d), rnd(rng, B, H, T, d), rnd(rng, B, H, T, d), rnd(rng, B, H, T, d)
+    O, _ = attention_forward(q, k, v)
+    base = attention_backward(q, k, v, dO)
+    for a, b in zip(attention_backward(q, k, v, dO, o_stored=O), base):
+        np.testing.assert_allclose(a, b, atol=1e-15)
+    dlt = 1e-3 * rnd(rng, B, H, T, d)
+    dQ, dK, dV = attention_backward(q, k, v, dO, o_stored=O + dlt)
+    np.testing.assert_array_equal(dV, base[2])
+    scale = 1.0 / math.sqrt(d)
+    for h in range(H):
+        P = np.zeros((T, T))
+        for i in range(T):
+            sc = [scale * float(q[0, h, i] @ k[0, h, j]) for j in range(i + 1)]
+            m = max(sc)
+            e = [math.exp(x - m) for x in sc]
+            P[i, :i + 1] = np.array(e) / sum(e)
+        dD = (dO[0, h] * dlt[0, h]).sum(-1)
+        np.testing.assert_allclose(dQ[0, h] - base[0][0, h], -scale * dD[:, None] * (P @ k[0, h]),
+                                   atol=1e-13)
+        np.testing.assert_allclose(dK[0, h] - base[1][0, h], -scale * P.T @ (dD[:, None] * q[0, h]),
+                                   atol=1e-13)
+    for flags in FLAG_SETS:
+        O, _ = attention_forward(q, k, v, **flags)
+        b0 = attention_backward(q, k, v, dO, **flags)
+        b1 = attention_backward(q, k, v, dO, o_stored=O + dlt, **flags)
+        b2 = attention_backward(q, k, v, dO, o_stored=O + 2 * dlt, **flags)
+        np.testing.assert_array_equal(b1[2], b0[2])
+        for x0, x1, x2 in zip(b0[:2], b1[:2], b2[:2]):
+            np.testing.assert_allclose(x2 - x0, 2 * (x1 - x0), atol=1e-13)
+
+
 def test_plain_attention_dk_sums_to_zero():
     """Without RoPE/cap/norm, adding a constant vector to every key shifts each score row by a
     constant, which softmax ignores: sum_j dK_j = 0."""
