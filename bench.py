@@ -336,8 +336,7 @@ def main():
         od = torch.empty_like(tq)
         opts = opts_of(wd)
         cfg = bd.make_decode_cfg(wd.B, wd.Hq, wd.Hkv, wd.D, wd.T, opts)
-        wsd = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg))),
-                          dtype=torch.uint8, device=dev)
+        wsd = bd.decode_workspace(wd.B, wd.Hq, wd.Hkv, wd.D, wd.T, opts)
         n = args.decode_iters
 
         def dec(i):
@@ -374,8 +373,7 @@ def main():
         os_ = torch.empty_like(tqs)
         opts_s = opts_of(ws)
         cfg_s = bd.make_decode_cfg(ws.B, ws.Hq, ws.Hkv, ws.D, ws.T, opts_s)
-        wss = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg_s))),
-                          dtype=torch.uint8, device=dev)
+        wss = bd.decode_workspace(ws.B, ws.Hq, ws.Hkv, ws.D, ws.T, opts_s)
         for _ in range(10):
             bd.attn_decode(tqs, tks, tvs, tls, opts_s, out=os_, workspace=wss)
         torch.cuda.synchronize()
@@ -402,8 +400,7 @@ def main():
         ol = torch.empty_like(tql)
         opts_l = opts_of(wl)
         cfg_l = bd.make_decode_cfg(wl.B, wl.Hq, wl.Hkv, wl.D, wl.T, opts_l)
-        wsl = torch.empty(int(bd.lib().attn_decode_workspace_bytes(ctypes.byref(cfg_l))),
-                          dtype=torch.uint8, device=dev)
+        wsl = bd.decode_workspace(wl.B, wl.Hq, wl.Hkv, wl.D, wl.T, opts_l)
 
         def dec_l(i):
             kcc, vcc = copies_l[i % len(copies_l)]

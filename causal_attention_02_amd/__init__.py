@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     attn_extend,
     attn_fwd,
     bwd_workspace_bytes,
+    decode_workspace,
+    device_info,
     dropout_mask_bytes,
     fwd_workspace_bytes,
     lib,

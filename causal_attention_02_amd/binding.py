@@ -25,7 +25,7 @@ EXPORTED = [
     "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
     "attn_trace_enable", "attn_trace_read", "attn_dropout_mask_bytes", "attn_dropout_mask",
     "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_leftpad", "attn_extend_leftpad",
-    "attn_bwd_khat", "attn_device_info",
+    "attn_bwd_khat", "attn_device_info", "attn_decode_ticket_bytes",
 ]
 
 
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_packed_workspace_bytes.restype = sz
         L.attn_decode_workspace_bytes.argtypes = [dcfgp]
         L.attn_decode_workspace_bytes.restype = sz
+        L.attn_decode_ticket_bytes.argtypes = [dcfgp]
+        L.attn_decode_ticket_bytes.restype = sz
         L.attn_check_cfg.argtypes = [cfgp, ctypes.c_int]
         L.attn_check_cfg.restype = ctypes.c_int
         L.attn_check_decode_cfg.argtypes = [dcfgp]
@@ -238,6 +240,17 @@ def _workspace(nbytes, device, ws):
             raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {nbytes} needed")
         return ws
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode_workspace(B, Hq, Hkv, D, Lmax, opts: AttnOptions | None = None, split_len: int = 0,
+                     device="cuda"):
+    """A zero-filled decode workspace for these sizes (its ticket counters must start at zero;
+    every attn_decode call leaves them zero, so it can be reused by later calls)."""
+    torch = _torch()
+    cfg = make_decode_cfg(B, Hq, Hkv, D, Lmax, opts or AttnOptions(), split_len)
+    _check(lib().attn_check_decode_cfg(ctypes.byref(cfg)), "decode_workspace")
+    n = int(lib().attn_decode_workspace_bytes(ctypes.byref(cfg)))
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def fwd_workspace_bytes(B, T, Hq, Hkv, D, opts: AttnOptions, dtype=ATTN_BF16) -> int:
@@ -416,7 +429,13 @@ def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None,
     _need(o, q.shape, bf, "out")
     cfg = make_decode_cfg(B, Hq, Hkv, D, Lmax, opts, split_len)
     _check(lib().attn_check_decode_cfg(ctypes.byref(cfg)), "attn_decode")
-    ws = _workspace(int(lib().attn_decode_workspace_bytes(ctypes.byref(cfg))), q.device, workspace)
+    nws = int(lib().attn_decode_workspace_bytes(ctypes.byref(cfg)))
+    if workspace is None:
+        # The ticket counters at its start must be zero (a caller-owned workspace keeps them
+        # zero from call to call; see decode_workspace).
+        ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=q.device)
+    else:
+        ws = _workspace(nws, q.device, workspace)
     if cache_start is not None:
         _need(cache_start, (B,), torch.int32, "cache_start")
         st = lib().attn_decode_leftpad(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),

@@ -134,23 +134,32 @@ int check_ecfg(const attn_extend_cfg* c) {
 
 float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
 
-// Default chunking: enough (b, kv head, head subset, chunk) workgroups to cover about 256
-// compute units even if every cache were full; one chunk per sequence when the batch alone
-// does that (then no merge pass is needed).  At most 16 chunks per sequence: the merge reads
-// the chunks of a row one after another, and beyond that it costs more than it saves.
+// (b, kv head, head subset) units of a decode call: each owns one ticket counter.
+long decode_units(const attn_decode_cfg* c) {
+  return (long)c->B * c->Hkv * (c->Hq / c->Hkv / decode_heads_per_block(c->Hq / c->Hkv, c->D));
+}
+
+// Default chunking.  A batch whose units alone give a workgroup to every compute unit streams
+// each cache in one chunk: every chunk pays the latency of its cache length and first rows
+// before it streams, and measured at 64 sequences of U{256..2048} rows, any split (64 to 1024
+// rows) was slower than none.  Smaller batches are cut into chunks (64 rows at least) so that
+// full caches would give about four workgroups per compute unit.
 int decode_split_len(const attn_decode_cfg* c) {
   if (c->split_len > 0) return c->split_len;
-  const long units = (long)c->B * c->Hkv * (c->Hq / c->Hkv / decode_heads_per_block(c->Hq / c->Hkv, c->D));
-  const long want = units >= 256 ? 1 : (256 + units - 1) / units;
-  long len = c->Lmax > 0 ? (c->Lmax + want - 1) / want : 64;
-  len = std::max(len, (c->Lmax + 15L) / 16);
-  len = (len + 63) / 64 * 64;
-  return (int)(len > 0 ? len : 64);
+  const long units = decode_units(c);
+  if (units >= 256 || c->Lmax <= 64) return c->Lmax > 0 ? (c->Lmax + 63) / 64 * 64 : 64;
+  const long len = ((long)c->Lmax * units + 1023) / 1024;
+  return (int)std::max(64L, (len + 63) / 64 * 64);
 }
 
 int decode_nsplit(const attn_decode_cfg* c) {
   const int sl = decode_split_len(c);
   return c->Lmax > 0 ? (c->Lmax + sl - 1) / sl : 1;
+}
+
+// The decode grid is one dimension of nsplit * units workgroups.
+bool decode_grid_fits(const attn_decode_cfg* c) {
+  return (int64_t)decode_nsplit(c) * decode_units(c) <= INT32_MAX;
 }
 
 // Workspace layouts (each region 256-byte aligned), when RoPE or QK-norm is on:
@@ -195,8 +204,11 @@ bool drop_params(float p, uint32_t* thr, float* scale) {
   return true;
 }
 
+// Decode workspace: [tickets: one uint32 per unit][partials B*Hq*nsplit*(D+2) f32].  The
+// ticket region must hold zeros before the first call; every call leaves it zero.
+size_t dec_count_bytes(const attn_decode_cfg* c) { return align_up((size_t)decode_units(c) * 4); }
 size_t dec_ws(const attn_decode_cfg* c) {
-  return align_up((size_t)c->B * c->Hq * decode_nsplit(c) * (c->D + 2) * 4);
+  return dec_count_bytes(c) + align_up((size_t)c->B * c->Hq * decode_nsplit(c) * (c->D + 2) * 4);
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ELAUNCH; }
@@ -234,6 +246,9 @@ size_t attn_bwd_packed_workspace_bytes(const attn_cfg* cfg) {
 }
 size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg) {
   return check_dcfg(cfg) == ATTN_OK ? dec_ws(cfg) : 0;
+}
+size_t attn_decode_ticket_bytes(const attn_decode_cfg* cfg) {
+  return check_dcfg(cfg) == ATTN_OK ? dec_count_bytes(cfg) : 0;
 }
 
 // Forward and backward bodies; `ids` (segment ids [B, T], or null) selects packed rows, whose
@@ -434,9 +449,11 @@ static int decode_impl(const attn_decode_cfg* c, const void* q, const void* k_ca
   if (c->B == 0) return ATTN_OK;
   if (!q || !o || !cache_len) return ATTN_EINVAL;
   if (c->Lmax > 0 && (!k_cache || !v_cache)) return ATTN_EINVAL;
+  if (!decode_grid_fits(c)) return ATTN_EUNSUPPORTED;
   const size_t need = dec_ws(c);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
-  DecodeParams p{q, k_cache, v_cache, cache_len, start, o, (float*)ws, c->B, c->Hq, c->Hkv,
+  DecodeParams p{q, k_cache, v_cache, cache_len, start, o,
+                 (float*)((char*)ws + dec_count_bytes(c)), (unsigned*)ws, c->B, c->Hq, c->Hkv,
                  c->D, c->Lmax, decode_split_len(c), decode_nsplit(c),
                  eff_scale(c->scale, c->D), c->softcap, c->rope, c->rope_base, c->qk_norm,
                  c->norm_eps};
@@ -472,6 +489,8 @@ int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, co
                 const int32_t* cache_len, void* o, void* ws, size_t ws_bytes, void* stream) {
   return decode_impl(c, q, k_cache, v_cache, nullptr, cache_len, o, ws, ws_bytes, stream);
 }
+
+
 
 int attn_decode_leftpad(const attn_decode_cfg* c, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_start, const int32_t* cache_len,

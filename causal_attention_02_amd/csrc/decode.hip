@@ -9,15 +9,24 @@
 // The work is HBM-bound (about 2 flops per byte), so it runs on the vector ALUs with
 // coalesced 16-byte loads, not on MFMA:
 //  * split kernel: one 4-wave workgroup per (chunk of split_len cache rows, b, kv head, head
-//    subset), two resident per CU.  Four lanes share one row (each owns D/4 elements: 64
-//    contiguous bytes per quad and load); a wave covers 16 rows per step, and the chunk is
-//    streamed in passes
-//    through a two-stage register pipeline (the loads of the next pass are in flight while
-//    the current one computes).  Each quad keeps a running (max, sum, output) for every
-//    query head of the GQA group (K and V are read once per KV head); quads and waves are
-//    merged (LSE-weighted) into one partial (m, l, o) per chunk.
-//  * combine kernel: merges the chunks of each (b, h): with M = max m_s,
-//    o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)  -- an exact identity of softmax.
+//    subset).  LPR lanes share one row, each owning D/LPR elements in 8- or 16-byte granules
+//    interleaved so that each load instruction reads one contiguous span of every row it
+//    touches; the chunk is streamed in passes of NW * 2 * 64 / LPR rows through a two-stage
+//    register pipeline (the loads of the next pass are in flight while the current one
+//    computes).  A whole cache per workgroup (the batch fills the GPU) uses four lanes per
+//    row and 16-byte loads.  Chunked caches use eight lanes per row: the per-lane buffers
+//    halve, four workgroups fit per CU, and the memory latency that starts each chunk (cache
+//    length, then the first rows) hides behind the other workgroups' streams.  Each lane keeps a
+//    running (max, sum, output) for every query head of the GQA group (K and V are read once
+//    per KV head); lanes and waves are merged (LSE-weighted) into one partial per chunk.
+//  * merge, in the same kernel: a sequence's active rows span n chunks (fixed split_len, so
+//    every workgroup streams about the same number of rows whatever the cache lengths).  With
+//    n = 1 the chunk writes the output itself.  Otherwise each chunk stores its partial
+//    (m, l, o), publishes it (agent-scope release) and takes a ticket from the (b, kv head,
+//    head subset) counter; the chunk that draws the last ticket reads the n partials
+//    (acquire), merges them -- with M = max m_s, o = sum_s o_s 2^(m_s - M) / sum_s l_s
+//    2^(m_s - M), an exact identity of softmax -- writes the output and sets the counter back
+//    to zero for the next call.
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,7 +41,8 @@ struct DecArgs {
   const int32_t* cache_len;
   const int32_t* cache_start;  // left padding rows per sequence (or null: none)
   bf16* o;
-  float* part;
+  float* part;      // [B, Hq, nsplit, D + 2] partials (m, l, o) of multi-chunk sequences
+  unsigned* count;  // [B * Hkv * head subsets] tickets; zero between calls
   int B, Hq, Hkv, Lmax, split_len, nsplit;
   ScoreCoef sc;    // score transform (mode chosen on the host)
   float scale;
@@ -46,6 +56,15 @@ __device__ __forceinline__ int active_end(const DecArgs& a, int b) {
 }
 __device__ __forceinline__ int active_first(const DecArgs& a, int b, int L) {
   return a.cache_start ? min(max(a.cache_start[b], 0), L) : 0;
+}
+
+// Device-coherent (agent-scope) store and load of a partial: performed where every compute
+// unit sees them, without the cache-wide write-back a release fence costs.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Waves per split workgroup: four, with two workgroups resident per CU, so one streams while
@@ -72,22 +91,29 @@ __device__ __forceinline__ void merge_state(RunState<NE>& s, float mp, float lp,
   s.m = mn;
 }
 
-__device__ __forceinline__ float dpp_ror(float x, int ctrl_is_8) {
-  const int v = __float_as_int(x);
-  return __int_as_float(ctrl_is_8 ? __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false)
-                                  : __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false));
+// Rotation by 4 or 8 lanes inside each row of 16 (DPP row_ror:4 / row_ror:8).
+template <int R>
+__device__ __forceinline__ float dpp_ror(float x) {
+  static_assert(R == 4 || R == 8, "row rotations by 4 or 8 lanes");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), R == 4 ? 0x124 : 0x128,
+                                                    0xf, 0xf, false));
 }
 
-// All-reduce of the states over the 16 lanes that share (lane & 3): two DPP row rotations
-// (by 4 and 8 lanes) inside each row of 16, then swaps across rows (xor 16, xor 32).
-template <int NE>
-__device__ __forceinline__ void merge_quads(RunState<NE>& s) {
-#pragma unroll
-  for (int r8 = 0; r8 < 2; ++r8) {
+// All-reduce of the states over the 64 / LPR lanes that share (lane % LPR): DPP row rotations
+// by 4 (when LPR = 4) and 8 inside each row of 16 lanes, then swaps across rows (xor 16, 32).
+template <int NE, int LPR>
+__device__ __forceinline__ void merge_rows(RunState<NE>& s) {
+  if constexpr (LPR == 4) {
     float op[NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) op[e] = dpp_ror(s.o[e], r8);
-    merge_state<NE>(s, dpp_ror(s.m, r8), dpp_ror(s.l, r8), op);
+    for (int e = 0; e < NE; ++e) op[e] = dpp_ror<4>(s.o[e]);
+    merge_state<NE>(s, dpp_ror<4>(s.m), dpp_ror<4>(s.l), op);
+  }
+  {
+    float op[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) op[e] = dpp_ror<8>(s.o[e]);
+    merge_state<NE>(s, dpp_ror<8>(s.m), dpp_ror<8>(s.l), op);
   }
   const int lane = threadIdx.x & 63;
   {
@@ -116,13 +142,36 @@ __device__ __forceinline__ void merge_quads(RunState<NE>& s) {
   }
 }
 
-template <int D, int HPB, int MODE>
-__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs a) {
+// Lane map of one cache row: LPR lanes (4 or 8), lane j owning granules j, j + LPR, ... of GB
+// bytes (16 when the row's 16-byte granules divide evenly among the lanes, else 8), so granule
+// k of all LPR lanes is one contiguous span of the row.  Element e of granule k of lane j is
+// head-dim index (j + LPR k) EPG + e.  Four lanes per row give 16-byte loads; eight halve the
+// per-lane buffers (more workgroups per CU).
+template <int D, int LPR>
+struct RowMap {
+  static constexpr int GB = ((D * 2 / 16) % LPR == 0) ? 16 : 8;
+  static constexpr int EPG = GB / 2;        // elements per granule
+  static constexpr int NG = D / EPG / LPR;  // granules per lane
+  static constexpr int NE = NG * EPG;       // elements per lane (D / LPR)
+  typedef __bf16 G __attribute__((ext_vector_type(EPG)));
+  static __device__ __forceinline__ int dim(int j, int k, int e) { return (j + LPR * k) * EPG + e; }
+  static_assert(LPR * NG * EPG == D, "the LPR lanes' granules tile the row exactly");
+};
+
+// Workgroups resident per CU: two with four lanes per row; with eight, four (three when the
+// group's heads hold 256 or more output elements per row).
+template <int D, int HPB, int LPR>
+constexpr int dec_min_blocks() { return LPR == 4 ? 2 : (HPB * D >= 256 ? 3 : 4); }
+
+template <int D, int HPB, int MODE, int LPR>
+__global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) void decode_split_kernel(DecArgs a) {
   constexpr int NW = kDecWaves;
-  constexpr int NU = D / 32;      // 16-byte chunks per lane per row
-  constexpr int NE = NU * 8;      // output elements per lane and head
+  typedef RowMap<D, LPR> RM;
+  constexpr int NG = RM::NG, EPG = RM::EPG;
+  constexpr int NE = RM::NE;      // output elements per lane and head
   constexpr int NSTEP = 2;        // rows per lane per pass (a pair: one dot2 per element)
-  constexpr int kRowsPerWave = 16 * NSTEP;
+  constexpr int kRowsPerStep = 64 / LPR;  // rows a wave covers per step
+  constexpr int kRowsPerWave = kRowsPerStep * NSTEP;
   constexpr int kPass = NW * kRowsPerWave;  // rows per workgroup pass
   __shared__ float sq[HPB][D];
   __shared__ float sm[NW][HPB], sl[NW][HPB];
@@ -130,48 +179,75 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
 
   const int G = a.Hq / a.Hkv;
   const int nsub = G / HPB;
-  const int split = blockIdx.x;
-  const int y = blockIdx.y;
+  // Workgroup i runs on XCD i % 8.  Chunk `split` of unit y is placed so that every XCD gets
+  // each chunk index of an eighth of the units, and a unit's chunks rotate over the XCDs:
+  // the first chunks (active for every sequence) and the last ones (active only for long
+  // caches) are spread evenly instead of landing on a few XCDs.
+  const int units = a.B * a.Hkv * nsub;
+  int split, y;
+  if ((units & 7) == 0) {
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    split = k % a.nsplit;
+    y = 8 * (k / a.nsplit) + ((xcd + split) & 7);
+  } else {
+    y = blockIdx.x % units;
+    split = blockIdx.x / units;
+  }
   const int hs = y % nsub;
   const int bg = y / nsub;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int h0 = g * G + hs * HPB;
+  // The raw query pair of this lane (wave hh < HPB holds head h0 + hh), loaded before anything
+  // waits on the cache length, so its latency overlaps that of the length.
+  const int half = D / 2;
+  const bool qact = w < HPB && lane < half;
+  float x1 = 0.f, x2 = 0.f;
+  if (qact) {
+    const bf16* qr = a.q + ((int64_t)b * a.Hq + h0 + w) * D;
+    x1 = from_bf16(qr[lane]);
+    x2 = from_bf16(qr[lane + half]);
+  }
   const int L = active_end(a, b);
   const int first = active_first(a, b, L);
   const int c0 = split * a.split_len;  // this chunk's rows: [c0, c0 + split_len) & [first, L)
   const int start = max(c0, first);
   const int stop = min(L, c0 + a.split_len);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int h0 = g * G + hs * HPB;
+  // Chunks s_first .. s_first + nact - 1 hold the active rows [first, L) (none if first == L).
+  const int s_first = first / a.split_len;
+  const int nact = first < L ? (L - 1) / a.split_len - s_first + 1 : 0;
   if (start >= stop) {
-    // No active row in this chunk.  With a single chunk per sequence (an empty active
-    // range) the output row is written here: zeros.
-    if (a.nsplit == 1)
+    // No active row in this chunk.  For an empty active range the first chunk writes the
+    // output row: zeros.
+    if (nact == 0 && split == 0)
       for (int t = tid; t < HPB * D; t += 64 * NW)
         a.o[((int64_t)b * a.Hq + h0 + t / D) * D + t % D] = to_bf16(0.f);
     return;
   }
   const int npass = (stop - start + kPass - 1) / kPass;
 
-  const int s4 = lane & 3;   // this lane's quarter of a row
-  const int rq = lane >> 2;  // row within a 16-row step
-  const bf16* kb = a.kc + (int64_t)bg * a.Lmax * D + 8 * s4;
-  const bf16* vb = a.vc + (int64_t)bg * a.Lmax * D + 8 * s4;
+  const int j8 = lane % LPR;  // this lane's part of a row
+  const int rq = lane / LPR;  // row within a step
+  const bf16* kb = a.kc + (int64_t)bg * a.Lmax * D;
+  const bf16* vb = a.vc + (int64_t)bg * a.Lmax * D;
   const int row0 = start + kRowsPerWave * w + rq;  // this lane's row in pass 0, step 0
 
   // Loads of one pass.  Rows past `stop` read row stop - 1 (in bounds, weight 0); this also
   // covers the prefetch issued past the last pass, so every load is unconditional and the
   // compiler waits for exactly the older pass.
+  typedef typename RM::G Gv;
   struct Buf {
-    bf16x8 k[NSTEP][NU], v[NSTEP][NU];
+    Gv k[NSTEP][NG], v[NSTEP][NG];
   };
   auto load = [&](Buf& bu, int pass) {
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      const int64_t off = (int64_t)min(row0 + kPass * pass + 16 * st, stop - 1) * D;
+      const int64_t off = (int64_t)min(row0 + kPass * pass + kRowsPerStep * st, stop - 1) * D;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        bu.k[st][u] = ld16<bf16x8>(kb + off + 32 * u);
-        bu.v[st][u] = ld16<bf16x8>(vb + off + 32 * u);
+      for (int u = 0; u < NG; ++u) {
+        // Granule u of this lane: elements RM::dim(j8, u, 0) .. + EPG - 1 of the row (< D).
+        bu.k[st][u] = *reinterpret_cast<const Gv*>(kb + off + RM::dim(j8, u, 0));
+        bu.v[st][u] = *reinterpret_cast<const Gv*>(vb + off + RM::dim(j8, u, 0));
       }
     }
   };
@@ -182,33 +258,28 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
   // Query prologue while the first loads are in flight: wave hh rotates (position
   // L - 1 - first) and normalises head h0 + hh.
   if (w < HPB) {
-    const int half = D / 2;
-    const bool act = lane < half;
-    const bf16* qr = a.q + ((int64_t)b * a.Hq + h0 + w) * D;
-    float x1 = act ? from_bf16(qr[lane]) : 0.f;
-    float x2 = act ? from_bf16(qr[lane + half]) : 0.f;
-    if (a.rp.rope && act) rope_pair(x1, x2, L - 1 - first, a.rp.omega_rev[lane], false);
+    if (a.rp.rope && qact) rope_pair(x1, x2, L - 1 - first, a.rp.omega_rev[lane], false);
     if (a.rp.qk_norm) {
       const float inv = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / (float)D + a.rp.eps);
       x1 *= inv;
       x2 *= inv;
     }
-    if (act) {
+    if (qact) {
       sq[w][lane] = x1;
       sq[w][lane + half] = x2;
     }
   }
   __syncthreads();
-  // q^ of this lane's row quarter, as bf16 pairs for v_dot2_f32_bf16 against the cached keys.
-  bf16x2 qv[HPB][NU * 4];
+  // q^ of this lane's eighth of a row, as bf16 pairs for v_dot2_f32_bf16 against the keys.
+  bf16x2 qv[HPB][NE / 2];
 #pragma unroll
   for (int hh = 0; hh < HPB; ++hh)
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < NG; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[hh][4 * u + e][0] = to_bf16(sq[hh][32 * u + 8 * s4 + 2 * e]);
-        qv[hh][4 * u + e][1] = to_bf16(sq[hh][32 * u + 8 * s4 + 2 * e + 1]);
+      for (int e = 0; e < EPG / 2; ++e) {
+        qv[hh][u * EPG / 2 + e][0] = to_bf16(sq[hh][RM::dim(j8, u, 2 * e)]);
+        qv[hh][u * EPG / 2 + e][1] = to_bf16(sq[hh][RM::dim(j8, u, 2 * e + 1)]);
       }
 
   RunState<NE> st_[HPB];
@@ -228,19 +299,19 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
     float yv[NSTEP][HPB];
 #pragma unroll
     for (int stp = 0; stp < NSTEP; ++stp) {
-      const bool valid = row0 + kPass * pass + 16 * stp < stop;
+      const bool valid = row0 + kPass * pass + kRowsPerStep * stp < stop;
 #pragma unroll
       for (int hh = 0; hh < HPB; ++hh) {
         float dot = 0.f;
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+        for (int u = 0; u < NG; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < EPG / 2; ++e) {
             const bf16x2 kp = {bu.k[stp][u][2 * e], bu.k[stp][u][2 * e + 1]};
-            dot = __builtin_amdgcn_fdot2_f32_bf16(qv[hh][4 * u + e], kp, dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(qv[hh][u * EPG / 2 + e], kp, dot, false);
           }
-        dot += __shfl_xor(dot, 1, 64);
-        dot += __shfl_xor(dot, 2, 64);
+#pragma unroll
+        for (int x = 1; x < LPR; x <<= 1) dot += __shfl_xor(dot, x, 64);
         const float yy = score_y<MODE, false>(dot, a.sc, 0.f, nullptr);
         yv[stp][hh] = valid ? yy : kNegBig;
       }
@@ -248,9 +319,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
     // Value pairs (row 0, row 1) per element, shared by all heads.
     bf16x2 vp[NE];
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < NG; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vp[8 * u + e] = bf16x2{bu.v[0][u][e], bu.v[1][u][e]};
+      for (int e = 0; e < EPG; ++e) vp[EPG * u + e] = bf16x2{bu.v[0][u][e], bu.v[1][u][e]};
 #pragma unroll
     for (int hh = 0; hh < HPB; ++hh) {
       RunState<NE>& S = st_[hh];
@@ -278,10 +349,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
     compute(b1, pass + 1);
   }
 
-  // Merge the 16 lanes of each wave that own the same quarter of the rows, then the waves.
+  // Merge the lanes of each wave that own the same part of the rows, then the waves.
 #pragma unroll
-  for (int hh = 0; hh < HPB; ++hh) merge_quads<NE>(st_[hh]);
-  if (lane < 4) {
+  for (int hh = 0; hh < HPB; ++hh) merge_rows<NE, LPR>(st_[hh]);
+  if (lane < LPR) {
 #pragma unroll
     for (int hh = 0; hh < HPB; ++hh) {
       if (lane == 0) {
@@ -289,9 +360,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
         sl[w][hh] = st_[hh].l;
       }
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
+      for (int u = 0; u < NG; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) so[w][hh][32 * u + 8 * s4 + e] = st_[hh].o[8 * u + e];
+        for (int e = 0; e < EPG; ++e) so[w][hh][RM::dim(j8, u, e)] = st_[hh].o[EPG * u + e];
     }
   }
   __syncthreads();
@@ -307,83 +378,92 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_split_kernel(DecArgs
       lt += sl[ww][hh] * f;
       ot += so[ww][hh][d] * f;
     }
-    if (a.nsplit == 1) {
+    if (nact == 1) {
       // The only chunk of this sequence: write the normalised output directly.
       a.o[((int64_t)b * a.Hq + h0 + hh) * D + d] = to_bf16(ot / lt);
     } else {
       float* pp = a.part + (((int64_t)b * a.Hq + h0 + hh) * a.nsplit + split) * (D + 2);
-      pp[2 + d] = ot;
+      coherent_store(pp + 2 + d, ot);
       if (d == 0) {
-        pp[0] = M;
-        pp[1] = lt;
+        coherent_store(pp, M);
+        coherent_store(pp + 1, lt);
       }
     }
   }
-}
-
-// One wave per (b, h), four per block.  Lanes read the chunks' (m, l) in parallel and the
-// wave reduces them; then each lane sums two output columns over the chunks.
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= a.B * a.Hq) return;
-  const int lane = threadIdx.x & 63;
-  const int b = wid / a.Hq;
-  const int L = active_end(a, b);
-  const int first = active_first(a, b, L);
-  // Chunks s0 .. n - 1 hold active rows (none when first == L); only they wrote partials.
-  const int n = (L + a.split_len - 1) / a.split_len;
-  const int s_first = first < L ? first / a.split_len : n;
-  const float* pp = a.part + ((int64_t)wid * a.nsplit + s_first) * (D + 2);
-  const int nact = n - s_first;
-  const bool act = 2 * lane < D;
-  float M = kNegBig;
-  for (int s = lane; s < nact; s += 64) M = fmaxf(M, pp[s * (D + 2)]);
+  if (nact == 1) return;
+  // Publish the partial, then take a ticket; the last of the nact chunks merges.  The partials
+  // travel only through device-coherent stores and loads, so publishing them needs no
+  // cache-wide write-back: each wave waits until its stores are performed, the barrier joins
+  // the waves, and only then is the ticket drawn.
+  __shared__ unsigned ticket;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  unsigned* cnt = a.count + y;
+  if (tid == 0) ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (ticket != (unsigned)(nact - 1)) return;
+  // Merge in batches of MB chunks: a batch's loads are all issued before any is used (indices
+  // past the last chunk re-read it with weight 0), so the merge waits for one memory round
+  // trip per batch, not per chunk.
+  constexpr int MB = 8;
+  for (int t = tid; t < HPB * D; t += 64 * NW) {
+    const int hh = t / D, d = t - hh * D;
+    const float* pp = a.part + (((int64_t)b * a.Hq + h0 + hh) * a.nsplit + s_first) * (D + 2);
+    float M = kNegBig, lt = 0.f, ot = 0.f;
+    for (int s0 = 0; s0 < nact; s0 += MB) {
+      float mv[MB], lv[MB], ov[MB];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  float lt = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s0 = 0; s0 < nact; s0 += 64) {
-    const int cnt = min(64, nact - s0);
-    const float* ps = pp + (s0 + lane) * (D + 2);
-    const float f = lane < cnt ? exp2_fast(ps[0] - M) : 0.f;
-    if (lane < cnt) lt = fmaf(ps[1], f, lt);
-#pragma unroll 4
-    for (int s = 0; s < cnt; ++s) {
-      const float fs = __shfl(f, s, 64);
-      if (act) {
-        const float2 v = *reinterpret_cast<const float2*>(pp + (s0 + s) * (D + 2) + 2 + 2 * lane);
-        o0 = fmaf(v.x, fs, o0);
-        o1 = fmaf(v.y, fs, o1);
+      for (int j = 0; j < MB; ++j) {
+        const float* ps = pp + min(s0 + j, nact - 1) * (D + 2);
+        mv[j] = coherent_load(ps);
+        lv[j] = coherent_load(ps + 1);
+        ov[j] = coherent_load(ps + 2 + d);
       }
+      float mb = M;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) mb = fmaxf(mb, mv[j]);
+      const float r = exp2_fast(M - mb);
+      lt *= r;
+      ot *= r;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const float f = s0 + j < nact ? exp2_fast(mv[j] - mb) : 0.f;
+        lt = fmaf(lv[j], f, lt);
+        ot = fmaf(ov[j], f, ot);
+      }
+      M = mb;
     }
+    a.o[((int64_t)b * a.Hq + h0 + hh) * D + d] = to_bf16(ot / lt);
   }
-  lt = wave_sum(lt);
-  const float inv = nact > 0 ? 1.f / lt : 0.f;
-  if (act) {
-    bf16x2 r;
-    r[0] = to_bf16(o0 * inv);
-    r[1] = to_bf16(o1 * inv);
-    *reinterpret_cast<bf16x2*>(a.o + (int64_t)wid * D + 2 * lane) = r;
-  }
+  // Every chunk of this sequence has drawn its ticket: ready for the next call.
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int HPB, int MODE>
+template <int D, int HPB, int MODE, int LPR>
 hipError_t launch_split(const DecArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * (G / HPB)));
+  const dim3 grid((unsigned)(a.nsplit * a.B * a.Hkv * (G / HPB)));
   static const char* names[4] = {"decode_split_d32", "decode_split_d64", "decode_split_d96",
                                  "decode_split_d128"};
   TraceScope t(names[D / 32 - 1], s);
-  hipLaunchKernelGGL((decode_split_kernel<D, HPB, MODE>), grid, dim3(64 * kDecWaves), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, HPB, MODE, LPR>), grid, dim3(64 * kDecWaves), 0, s, a);
   return hipGetLastError();
+}
+
+// One chunk per cache: four lanes per row (16-byte loads; measured faster when each
+// workgroup streams a whole cache).  Chunked caches: eight lanes per row (four workgroups per
+// CU hide each chunk's start-up latency behind the others' streams).
+template <int D, int HPB, int MODE>
+hipError_t launch_split_lanes(const DecArgs& a, hipStream_t s) {
+  return a.nsplit == 1 ? launch_split<D, HPB, MODE, 4>(a, s) : launch_split<D, HPB, MODE, 8>(a, s);
 }
 
 template <int D, int HPB>
 hipError_t launch_split_mode(const DecArgs& a, int mode, hipStream_t s) {
-  if (mode == kScoreScale) return launch_split<D, HPB, kScoreScale>(a, s);
-  if (mode == kScoreCapPoly5) return launch_split<D, HPB, kScoreCapPoly5>(a, s);
-  if (mode == kScoreCapPoly) return launch_split<D, HPB, kScoreCapPoly>(a, s);
-  return launch_split<D, HPB, kScoreCapExp>(a, s);
+  if (mode == kScoreScale) return launch_split_lanes<D, HPB, kScoreScale>(a, s);
+  if (mode == kScoreCapPoly5) return launch_split_lanes<D, HPB, kScoreCapPoly5>(a, s);
+  if (mode == kScoreCapPoly) return launch_split_lanes<D, HPB, kScoreCapPoly>(a, s);
+  return launch_split_lanes<D, HPB, kScoreCapExp>(a, s);
 }
 
 template <int D>
@@ -402,11 +482,7 @@ hipError_t launch_decode_d(const DecArgs& a, int mode, hipStream_t s) {
     case 2: e = launch_split_mode<D, 2>(a, mode, s); break;
     default: e = launch_split_mode<D, 1>(a, mode, s); break;
   }
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  TraceScope t("decode_combine", s);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((a.B * a.Hq + 3) / 4)), dim3(256),
-                     0, s, a);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace
@@ -420,6 +496,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.cache_start = p.cache_start;
   a.o = (bf16*)p.o;
   a.part = p.part;
+  a.count = p.count;
   a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;

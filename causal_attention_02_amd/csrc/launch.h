@@ -184,6 +184,7 @@ struct DecodeParams {
   const int32_t* cache_start;  // left padding rows per sequence (null: none)
   void* o;              // [B, Hq, D]
   float* part;          // [B, Hq, nsplit, D + 2]
+  unsigned* count;      // [B * Hkv * head subsets], zero on entry and on exit
   int B, Hq, Hkv, D, Lmax, split_len, nsplit;
   float scale, softcap;
   int rope;

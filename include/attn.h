@@ -207,7 +207,8 @@ int attn_bwd_dropout(const attn_cfg* cfg, const void* q, const void* k, const vo
 
 /*
  * attn_decode -- one new query per sequence against its KV cache (split-K over the cache
- * length, then an LSE-weighted merge of the chunks).  bfloat16 only.
+ * length in chunks of cfg->split_len rows, then an LSE-weighted merge of a sequence's chunks
+ * by the last of them to finish).  bfloat16 only.
  *   q         [B, Hq, D] device, bf16 -- raw (un-rotated) query of the newest token
  *   k_cache   [B, Hkv, Lmax, D] device, bf16 -- keys already rotated (and normalised when
  *             qk_norm = 1); the newest token's key is already appended
@@ -215,8 +216,12 @@ int attn_bwd_dropout(const attn_cfg* cfg, const void* q, const void* k, const vo
  *   cache_len [B] device, int32 -- active rows L_b; only rows 0..L_b-1 are read.  Values
  *             are clamped to [0, Lmax] in the kernel; L_b = 0 yields a zero output row.
  *   o         [B, Hq, D] device, bf16 (written)
- *   ws        device workspace of ws_bytes >= attn_decode_workspace_bytes(cfg).
+ *   ws        device workspace of ws_bytes >= attn_decode_workspace_bytes(cfg).  Its first
+ *             attn_decode_ticket_bytes(cfg) bytes are ticket counters that must be ZERO before
+ *             the workspace is first used (e.g. allocated zero-filled); every call leaves them
+ *             zero again.  Calls that share a workspace must not overlap.
  */
+size_t attn_decode_ticket_bytes(const attn_decode_cfg* cfg);
 int attn_decode(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* cache_len, void* o, void* ws,
                 size_t ws_bytes, void* stream);

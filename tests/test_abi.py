@@ -72,17 +72,25 @@ def test_workspace_sizes(L):
     assert L.attn_fwd_workspace_bytes(ctypes.byref(plain)) == 0
     assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == 2 * rows * 4
     assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(Hq=5))) == 0  # invalid -> 0
-    # Default chunking: 64 x 4 (b, kv head) workgroups already cover the GPU -> one chunk.
+    # Decode: [tickets, one uint32 per (b, kv head, head subset)][partials B*Hq*nsplit*(D+2)
+    # f32], each region 256-byte aligned.
+    al = lambda x: (x + 255) // 256 * 256
+    # 64 x 4 units fill the GPU: one chunk per cache.
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(softcap=50.0, rope=True))
-    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 1 * 98 * 4
-    # One sequence: 4 (b, kv head) units would want 64 chunks; capped at 16 (256 rows each).
+    assert L.attn_decode_ticket_bytes(ctypes.byref(d)) == al(64 * 4 * 4)
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == al(64 * 4 * 4) + 64 * 8 * 1 * 98 * 4
+    # One sequence, 4 units: 64-row chunks (64 over a 4096-row cache).
     d = bd.make_decode_cfg(1, 8, 4, 96, 4096, bd.AttnOptions())
-    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 1 * 8 * 16 * 98 * 4
-    # A 256-row cache of one sequence keeps 4 chunks of 64 rows.
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == al(4 * 4) + 1 * 8 * 64 * 98 * 4
+    # 16 sequences x 4 units: 64 units, chunks of ceil(2048 * 64 / 1024) = 128 rows.
+    d = bd.make_decode_cfg(16, 8, 4, 96, 2048, bd.AttnOptions())
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == al(64 * 4) + 16 * 8 * 16 * 98 * 4
+    # A 256-row cache of one sequence, 12 units: 64-row chunks, so 48 workgroups.
     d = bd.make_decode_cfg(1, 12, 12, 64, 256, bd.AttnOptions())
-    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == (1 * 12 * 4 * 66 * 4 + 255) // 256 * 256
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == al(12 * 4) + al(1 * 12 * 4 * 66 * 4)
     d = bd.make_decode_cfg(64, 8, 4, 96, 2048, bd.AttnOptions(), split_len=128)
-    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == 64 * 8 * 16 * 98 * 4
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) == al(64 * 4 * 4) + 64 * 8 * 16 * 98 * 4
+    assert L.attn_decode_ticket_bytes(None) == 0
 
 
 def test_packed_workspace_and_validation(L):
@@ -260,3 +268,4 @@ def test_status_strings_and_trace(L):
 def test_device_info_rejects_null(L):
     """Host-only: a null output is rejected before the runtime is asked anything."""
     assert L.attn_device_info(0, None) == bd.ATTN_EINVAL
+

@@ -300,6 +300,33 @@ def test_decode_reads_only_active_rows_and_split_invariance():
         assert rel_l2(o, outs[0]) <= 4e-3
 
 
+def test_decode_tickets_return_to_zero():
+    """One zero-filled workspace over consecutive calls whose cache lengths change how many
+    chunks each sequence spans (and so which chunk merges): every output matches the oracle and
+    the ticket counters are zero after each call."""
+    import ctypes
+    import torch
+    from causal_attention_02_amd import binding as bd
+    w = WORKLOADS["gqa181m_decode"].with_(B=7, T=1100)
+    q, kc, vc, _ = make_decode_inputs(w)
+    opts = opts_of(w)
+    cfg = bd.make_decode_cfg(w.B, w.Hq, w.Hkv, w.D, w.T, opts, 128)
+    nt = int(bd.lib().attn_decode_ticket_bytes(ctypes.byref(cfg)))
+    assert nt >= 4 * w.B * w.Hkv
+    ws = bd.decode_workspace(w.B, w.Hq, w.Hkv, w.D, w.T, opts, split_len=128)
+    tq, tkc, tvc = (to_dev(x, torch.bfloat16) for x in (q, kc, vc))
+    kw = {k: v for k, v in oracle_kw(w).items() if k != "window"}
+    for lens in ([1100, 1, 128, 129, 0, 700, 255], [1, 1100, 129, 128, 5, 256, 1099],
+                 [640, 641, 1, 2, 3, 1100, 0]):
+        lens = np.array(lens, dtype=np.int32)
+        o = attn_decode(tq, tkc, tvc, torch.from_numpy(lens).to("cuda"), opts, split_len=128,
+                        workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[:nt].any().item(), lens
+        e = rel_l2(to_host(o), attention_decode(q, kc, vc, lens, **kw))
+        assert e <= TOL_O, (lens, e)
+
+
 def test_decode_matches_last_forward_row():
     """Decode over a cache of rotated keys equals the last row of the training forward."""
     import torch
@@ -789,7 +816,7 @@ def test_graph_replay_matches_eager():
     tqd, tkc, tvc = (to_dev(x, torch.bfloat16) for x in (qd, kc, vc))
     tl = torch.from_numpy(lens).to("cuda")
     od = torch.empty_like(tqd)
-    dec_ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    dec_ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")  # tickets start at zero
 
     def step():
         attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf)
