@@ -16,6 +16,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libcausal_attn.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_ELAUNCH = 0, -1, -2, -3, -4
+ATTN_ESCRATCH = -5
+DECODE_NOALLOC_MAX_BYTES = 8 << 20
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = [
@@ -25,7 +27,7 @@ EXPORTED = [
     "attn_fwd_packed", "attn_bwd_packed", "attn_decode", "attn_extend", "attn_status_str",
     "attn_trace_enable", "attn_trace_read", "attn_dropout_mask_bytes", "attn_dropout_mask",
     "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_leftpad", "attn_extend_leftpad",
-    "attn_bwd_khat", "attn_device_info", "attn_decode_ticket_bytes",
+    "attn_bwd_khat", "attn_device_info", "attn_decode_ticket_bytes", "attn_decode_noalloc",
 ]
 
 
@@ -124,6 +126,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_dropout.restype = ctypes.c_int
         L.attn_decode.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_decode.restype = ctypes.c_int
+        L.attn_decode_noalloc.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp]
+        L.attn_decode_noalloc.restype = ctypes.c_int
         L.attn_extend.argtypes = [ecfgp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_extend.restype = ctypes.c_int
         L.attn_decode_leftpad.argtypes = [dcfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -449,6 +453,27 @@ def attn_decode(q, k_cache, v_cache, cache_len, opts: AttnOptions | None = None,
                            _stream(stream))
     _check(st, "attn_decode")
     return o
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, cache_len, out, opts: AttnOptions | None = None, *,
+                        split_len=0, stream=None):
+    """attn_decode into a caller-given `out` with the library's static scratch as workspace:
+    nothing is allocated (no torch allocation either).  Same shapes as attn_decode."""
+    torch = _torch()
+    opts = opts or AttnOptions()
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    bf = torch.bfloat16
+    _need(q, (B, Hq, D), bf, "q")
+    _need(k_cache, (B, Hkv, Lmax, D), bf, "k_cache")
+    _need(v_cache, (B, Hkv, Lmax, D), bf, "v_cache")
+    _need(cache_len, (B,), torch.int32, "cache_len")
+    _need(out, q.shape, bf, "out")
+    cfg = make_decode_cfg(B, Hq, Hkv, D, Lmax, opts, split_len)
+    st = lib().attn_decode_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(cache_len), _ptr(out), _stream(stream))
+    _check(st, "attn_decode_noalloc")
+    return out
 
 
 @_on_stream

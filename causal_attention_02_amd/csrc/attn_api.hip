@@ -224,6 +224,7 @@ const char* attn_status_str(int s) {
     case ATTN_EUNSUPPORTED: return "unsupported configuration";
     case ATTN_EWORKSPACE: return "workspace missing or too small";
     case ATTN_ELAUNCH: return "kernel launch failed";
+    case ATTN_ESCRATCH: return "needs more than the static decode scratch";
   }
   return "unknown status";
 }
@@ -490,7 +491,52 @@ int attn_decode(const attn_decode_cfg* c, const void* q, const void* k_cache, co
   return decode_impl(c, q, k_cache, v_cache, nullptr, cache_len, o, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
 
+// ---------------------------------------------------------------------------------------
+// Allocation-free decode: the workspace is a statically sized device array.  The loader
+// zero-fills it, and every call leaves its ticket region zero again, so it starts each call
+// as attn_decode requires.  In host code `scratch` only names the symbol; its device address
+// is looked up once per device (hipGetSymbolAddress, with that device current) and only that
+// address is passed to kernels.
+// ---------------------------------------------------------------------------------------
+namespace {
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_NOALLOC_MAX_BYTES];
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+
+// This device's copy of `scratch` (null with the runtime's error when the lookup failed).
+void* scratch_for_device(int dev, hipError_t* err) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int attn_decode_noalloc(const attn_decode_cfg* c, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_len, void* o, void* stream) {
+  const int st = check_dcfg(c);
+  if (st != ATTN_OK) return st;
+  if (c->B == 0) return ATTN_OK;
+  if (dec_ws(c) > (size_t)ATTN_DECODE_NOALLOC_MAX_BYTES) return ATTN_ESCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ELAUNCH;
+  if (dev >= kScratchDevices) return ATTN_EUNSUPPORTED;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_for_device(dev, &e);
+  if (!ws) return ATTN_ELAUNCH;
+  return decode_impl(c, q, k_cache, v_cache, nullptr, cache_len, o, ws,
+                     (size_t)ATTN_DECODE_NOALLOC_MAX_BYTES, stream);
+}
 
 int attn_decode_leftpad(const attn_decode_cfg* c, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_start, const int32_t* cache_len,

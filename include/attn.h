@@ -51,7 +51,8 @@ typedef enum {
   ATTN_EINVAL = -1,       /* a null pointer, a negative or inconsistent size, Hq % Hkv != 0 ... */
   ATTN_EUNSUPPORTED = -2, /* valid but not implemented: D not in {32,64,96,128}, fp32 backward ... */
   ATTN_EWORKSPACE = -3,   /* workspace missing or smaller than the *_workspace_bytes() figure   */
-  ATTN_ELAUNCH = -4       /* the HIP runtime refused a launch                                   */
+  ATTN_ELAUNCH = -4,      /* the HIP runtime refused a launch                                   */
+  ATTN_ESCRATCH = -5      /* attn_decode_noalloc: the call needs more than its static scratch   */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -225,6 +226,21 @@ size_t attn_decode_ticket_bytes(const attn_decode_cfg* cfg);
 int attn_decode(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* cache_len, void* o, void* ws,
                 size_t ws_bytes, void* stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device memory (code
+ * recorded into a HIP graph, tight serving loops, harnesses that forbid allocation): the
+ * workspace is a static device array of ATTN_DECODE_NOALLOC_MAX_BYTES per GPU, held until the
+ * process ends, instead of a caller buffer.  Every other argument and rule is attn_decode's.
+ * Configurations whose attn_decode_workspace_bytes exceeds that size return ATTN_ESCRATCH
+ * before anything is enqueued.  The call allocates nothing (its first call on a device looks
+ * up that device's copy of the array once).  All calls on one GPU share the array: calls that
+ * overlap in time on one GPU (concurrent streams, or a graph replayed while another call
+ * runs) race and must not be issued.  The current device must be the stream's device.
+ */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES (8u << 20)
+int attn_decode_noalloc(const attn_decode_cfg* cfg, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_len, void* o, void* stream);
 
 /*
  * attn_extend -- S new tokens per sequence against its KV cache (the multi-token form of the

@@ -269,3 +269,12 @@ def test_device_info_rejects_null(L):
     """Host-only: a null output is rejected before the runtime is asked anything."""
     assert L.attn_device_info(0, None) == bd.ATTN_EINVAL
 
+
+def test_noalloc_decode_rejects_oversized_before_any_device_call(L):
+    """The static-scratch decode checks its size on the host: a configuration needing more
+    than the scratch returns ATTN_ESCRATCH (null pointers are never reached)."""
+    d = bd.make_decode_cfg(64, 8, 4, 96, 8192, bd.AttnOptions(), split_len=64)
+    assert L.attn_decode_workspace_bytes(ctypes.byref(d)) > bd.DECODE_NOALLOC_MAX_BYTES
+    assert L.attn_decode_noalloc(ctypes.byref(d), None, None, None, None, None, None) == \
+        bd.ATTN_ESCRATCH
+    assert L.attn_decode_noalloc(None, None, None, None, None, None, None) == bd.ATTN_EINVAL
