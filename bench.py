@@ -164,8 +164,9 @@ def main():
                 fn(i)
             torch.cuda.synchronize()
 
-    def train_case(w, steps, warmup, trace=False, ids=None):
-        """Time fwd + bwd; with w.dropout > 0 each step also draws a fresh keep mask."""
+    def train_case(w, steps, warmup, trace=False, ids=None, split=False):
+        """Time fwd + bwd; with w.dropout > 0 each step also draws a fresh keep mask; split:
+        the backward is attn_bwd_split."""
         q, k, v, dO = make_train_inputs(w)
         tids = None if ids is None else torch.from_numpy(ids).to(dev)
         tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(dO)
@@ -179,7 +180,8 @@ def main():
         cfg = bd.make_cfg(B, T, Hq, Hkv, D, opts, bd.ATTN_BF16)
         if tids is None:
             nf = bd.lib().attn_fwd_workspace_bytes(ctypes.byref(cfg))
-            nb = bd.lib().attn_bwd_workspace_bytes(ctypes.byref(cfg))
+            nb = (bd.lib().attn_bwd_split_workspace_bytes if split else
+                  bd.lib().attn_bwd_workspace_bytes)(ctypes.byref(cfg))
         else:
             nf = bd.lib().attn_fwd_packed_workspace_bytes(ctypes.byref(cfg))
             nb = bd.lib().attn_bwd_packed_workspace_bytes(ctypes.byref(cfg))
@@ -193,7 +195,8 @@ def main():
         calls = [0]
         # The backward takes k after RoPE / QK-norm from the forward's workspace (a training
         # step keeps it from the forward to the backward, as it keeps o and lse).
-        khat = wsf if ((w.rope or w.qk_norm) and tids is None and mask is None) else None
+        khat = wsf if ((w.rope or w.qk_norm) and tids is None and mask is None and not split) \
+            else None
 
         def step(_i=0):
             if mask is not None:
@@ -202,7 +205,7 @@ def main():
             bd.attn_fwd(tq, tk, tv, opts, out=o, lse=lse, workspace=wsf, segment_ids=tids,
                         dropout_p=p, dropout_mask=mask)
             bd.attn_bwd(tq, tk, tv, o, tdo, lse, opts, dq=dq, dk=dk, dv=dv, workspace=wsb,
-                        segment_ids=tids, dropout_p=p, dropout_mask=mask, khat=khat)
+                        segment_ids=tids, dropout_p=p, dropout_mask=mask, khat=khat, split=split)
 
         settle(step)
         for _ in range(warmup):
@@ -247,6 +250,15 @@ def main():
                         frac=achieved / PEAK_BF16_TFLOPS, traffic=measured_traffic(dom),
                         algorithmic_flops_per_launch=algo_per_pair[fam] * pairs)
         result["roofline"] = roof
+        # The same step with the split backward (dS stored by dK/dV, dQ from it), for the
+        # comparison of the two backward designs.
+        log(f"[bench] fwd+bwd {main_w.name} with attn_bwd_split")
+        ms_s, per_s, kern_s = train_case(main_w, max(args.steps // 2, 3), 2, trace=True,
+                                         split=True)
+        extra["gqa181m_train_split_bwd"] = dict(
+            ms_per_step=ms_s, tflops=train_flops(main_w) / (ms_s * 1e-3) / 1e12,
+            kernels_ms={n: round(t / c, 4) for n, (c, t) in kern_s.items()})
+        log(f"[bench] {main_w.name} split backward: {ms_s:.3f} ms/step")
         # MiniGPT shapes: the fp32 forward (B=2, T=128, 6 heads, d=32) and the bf16 training
         # batch (B=32) -- both far too small to fill the GPU; reported per call.
         w1 = WORKLOADS["minigpt_fwd_f32"]

@@ -174,7 +174,9 @@ size_t fwd_ws(const attn_cfg* c) {
   return align_up(nq * 4) + align_up(nk * 4);
 }
 
-size_t bwd_ws(const attn_cfg* c) {
+// Backward workspace without the dS fragments (packed rows and dropout recompute dS in the
+// dq pass).
+size_t bwd_ws_base(const attn_cfg* c) {
   const size_t rows = (size_t)c->B * c->Hq * c->T;
   size_t s = 2 * align_up(rows * 4);
   if (c->rope || c->qk_norm) {
@@ -183,6 +185,15 @@ size_t bwd_ws(const attn_cfg* c) {
   }
   return s;
 }
+
+size_t bwd_ws(const attn_cfg* c) { return bwd_ws_base(c); }
+
+// Split backward (attn_bwd_split): the base regions, then the dS fragments (bf16, the band of
+// the causal / window mask, 1 KB per 32 x 16 block).
+size_t ds_bytes(const attn_cfg* c) {
+  return align_up((size_t)c->B * c->Hq * (size_t)make_ds_band(c->T, c->window).frags * 1024);
+}
+size_t bwd_split_ws(const attn_cfg* c) { return bwd_ws_base(c) + ds_bytes(c); }
 
 // Packed rows: run starts and ends, [B, T] int32 each.
 size_t seg_ws(const attn_cfg* c) { return 2 * align_up((size_t)c->B * c->T * 4); }
@@ -243,7 +254,10 @@ size_t attn_fwd_packed_workspace_bytes(const attn_cfg* cfg) {
   return check_cfg(cfg, 0) == ATTN_OK ? fwd_ws(cfg) + seg_ws(cfg) : 0;
 }
 size_t attn_bwd_packed_workspace_bytes(const attn_cfg* cfg) {
-  return check_cfg(cfg, 1) == ATTN_OK ? bwd_ws(cfg) + seg_ws(cfg) : 0;
+  return check_cfg(cfg, 1) == ATTN_OK ? bwd_ws_base(cfg) + seg_ws(cfg) : 0;
+}
+size_t attn_bwd_split_workspace_bytes(const attn_cfg* cfg) {
+  return check_cfg(cfg, 1) == ATTN_OK ? bwd_split_ws(cfg) : 0;
 }
 size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg) {
   return check_dcfg(cfg) == ATTN_OK ? dec_ws(cfg) : 0;
@@ -306,16 +320,17 @@ static int fwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
 }
 
 // khat: k after RoPE / QK-norm as the forward used it (null: computed here).
+// split: the split backward (dS stored by the dK/dV pass, dQ from it); plain rows, no dropout.
 static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void* v,
                     const void* o, const void* dO, const float* lse, const int32_t* ids,
                     void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
                     const void* drop = nullptr, float dscale = 1.f,
-                    const void* khat = nullptr) {
+                    const void* khat = nullptr, bool split = false) {
   int st = check_cfg(c, 1);
   if (st != ATTN_OK) return st;
   if (c->B == 0 || c->T == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_EINVAL;
-  const size_t need = bwd_ws(c) + (ids ? seg_ws(c) : 0);
+  const size_t need = split ? bwd_split_ws(c) : ids ? bwd_ws(c) + seg_ws(c) : bwd_ws(c);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int64_t qrows = (int64_t)c->B * c->Hq * c->T, krows = (int64_t)c->B * c->Hkv * c->T;
@@ -355,6 +370,17 @@ static int bwd_impl(const attn_cfg* c, const void* q, const void* k, const void*
     p.seg_start = sst;
     p.seg_end = sen;
   }
+  if (split) {
+    // -D, LSE log2(e) and q^ in one pass; dK, dV with dS stored as fragments; dQ from them.
+    p.ds = (char*)ws + bwd_ws_base(c);
+    p.band = make_ds_band(c->T, c->window);
+    if (e == hipSuccess)
+      e = launch_bwd_prep(q, o, dO, lse, pro ? qh : nullptr, Dvec, L2, qrows, c->T, c->D, c->rope,
+                          c->rope_base, c->qk_norm, c->norm_eps, s);
+    if (e == hipSuccess) e = launch_bwd_dkdv(p, s);
+    if (e == hipSuccess) e = launch_bwd_dq_ds(p, s);
+    return launch_status(e);
+  }
   if (e == hipSuccess) e = launch_bwd_dq(p, s);
   if (e == hipSuccess) e = launch_bwd_dkdv(p, s);
   return launch_status(e);
@@ -377,6 +403,13 @@ int attn_bwd_khat(const attn_cfg* c, const void* q, const void* k, const void* v
   if (c && (c->rope || c->qk_norm) && c->B > 0 && c->T > 0 && !khat) return ATTN_EINVAL;
   return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream, nullptr,
                   1.f, khat);
+}
+
+int attn_bwd_split(const attn_cfg* c, const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return bwd_impl(c, q, k, v, o, dO, lse, nullptr, dq, dk, dv, ws, ws_bytes, stream, nullptr,
+                  1.f, nullptr, true);
 }
 
 int attn_fwd_packed(const attn_cfg* c, const void* q, const void* k, const void* v,

@@ -67,7 +67,19 @@ struct BwdArgs {
   float scale;
   ScoreCoef sc;
   RowPrologue rp;
+  bf16* ds;    // split backward: dS fragments (null: not exported / not used)
+  DsBand band;
 };
+
+// ---- dS fragments ----------------------------------------------------------------------------
+// Key blocks lo .. hi of 32-query block i, and the fragment index of (i, j) within a head.
+__device__ __forceinline__ int ds_lo(int i, const DsBand& d) {
+  return d.window > 0 ? max(0, 32 * i - d.window + 1) >> 4 : 0;
+}
+__device__ __forceinline__ int ds_hi(int i, const DsBand& d) { return min(2 * i + 1, d.nkb - 1); }
+__device__ __forceinline__ int64_t ds_frag(int i, int j, const DsBand& d) {
+  return d.stride == 0 ? (int64_t)i * (i + 1) + j : (int64_t)i * d.stride + (j - ds_lo(i, d));
+}
 
 // Store 4 consecutive values of a row (accumulator layout) as bf16.
 __device__ __forceinline__ void store4(bf16* p, const float* v) {
@@ -447,7 +459,8 @@ constexpr int kBMt = 64;    // queries per dkdv tile
 
 // Two waves per SIMD for D <= 64, and for D = 96 without dropout (its keep words and -D
 // values no longer fit the 256 registers two waves allow); one otherwise.
-template <int D, int MODE, bool DROP>
+// EXPORT: also store this pass's dS as fragments for bwd_dq_ds_kernel (the split backward).
+template <int D, int MODE, bool DROP, bool EXPORT>
 __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int LD = D + 8;
   constexpr int NS = D / 16;
@@ -463,6 +476,10 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
   // Dropout keep words of the tile's two 32-query blocks for the 128 keys: [block][key].
   __shared__ __attribute__((aligned(16))) uint32_t sM0[DROP ? 2 * kBNkv : 1];
   __shared__ __attribute__((aligned(16))) uint32_t sM1[DROP ? 2 * kBNkv : 1];
+  // Split backward: each wave's dS of the current tile, [32 keys][64 queries + 8] bf16, written
+  // in the accumulator layout and read back transposed into fragments (wave-private: no barrier).
+  constexpr int DSP = kBMt + 8;
+  __shared__ __attribute__((aligned(16))) bf16 sDS[EXPORT ? 4 * 32 * DSP : 1];
 
   const int T = a.T;
   const int nbg = a.B * a.Hkv;
@@ -566,6 +583,52 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
   const int trow = 4 * gl + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
+  // dS export.  stash(qb, t, v): v = dS of block qb, half t packed as bf16 (elements 0-3:
+  // queries 16 t + 4 gl + 0..3 of the block, 4-7: 16 t + 8 + 4 gl + 0..3) into this wave's
+  // [key][query] buffer.  export_ds(q0): after the tile, the transposing reads turn it into
+  // the fragments of (32-query block, 16-key block) pairs inside the band, stored whole.
+  static_assert(!(EXPORT && DROP), "dS export is for the plain backward");
+  // The lane's offsets into the buffer are recomputed from a fresh lane id at each use (the
+  // empty asm keeps them from being held in registers across the tile loop).
+  auto lane_id = []() __attribute__((always_inline)) {
+    int t = (int)__builtin_amdgcn_workitem_id_x();
+    asm volatile("" : "+v"(t));
+    return t;
+  };
+  auto stash = [&](int qb, int t, const bf16x8& v) __attribute__((always_inline)) {
+    if constexpr (EXPORT) {
+      const int id = lane_id(), ll = id & 63;
+      bf16* row = sDS + ((id >> 6) * 32 + (ll & 31)) * DSP + 4 * (ll >> 5) + 32 * qb + 16 * t;
+      *reinterpret_cast<bf16x4*>(row) = bf16x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<bf16x4*>(row + 8) = bf16x4{v[4], v[5], v[6], v[7]};
+    }
+  };
+  auto export_ds = [&](int hh, int q0) __attribute__((always_inline)) {
+    if constexpr (EXPORT) {
+      const int id = lane_id(), ll = id & 63, gq = ll >> 4, L = ll & 15;
+      // Loader role of this lane: key row 8 (gq / 2) + L / 4 (+ 4), query columns
+      // 16 (gq % 2) + 4 (L % 4) .. + 3 of the fragment's 16 x 32 window.
+      const bf16* src = sDS + ((id >> 6) * 32 + 8 * (gq >> 1) + (L >> 2)) * DSP +
+                        16 * (gq & 1) + 4 * (L & 3);
+      bf16* dst = a.ds + ((int64_t)(b * a.Hq + g * G + hh) * a.band.frags) * 512 + 8 * ll;
+#pragma unroll
+      for (int qf = 0; qf < 2; ++qf) {
+        const int i = (q0 >> 5) + qf;
+        if (i >= a.band.nqb) continue;
+        const int lo = ds_lo(i, a.band), hi = ds_hi(i, a.band);
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf) {
+          const int j = (kw0 >> 4) + kf;
+          if (j < lo || j > hi) continue;
+          const bf16* p0 = src + 16 * kf * DSP + 32 * qf;
+          const bf16x8 v = tr_read_pair(p0, p0 + 4 * DSP);
+          // Streamed past the L2, where this pass keeps its q^ / dO tiles.
+          __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(dst + ds_frag(i, j, a.band) * 512));
+        }
+      }
+    }
+  };
+
   // One q tile against this wave's 32 keys, operands in (sq, so, sl, sd), keep words in sm:
   // the two 32-query blocks one after the other.
   auto step_split = [&](int it, const bf16* sq, const bf16* so, const float* sl,
@@ -663,6 +726,7 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
           bf16x8 pb[2], dsb[2];
           pb[0] = pack8(sacc, 0);
           dsb[0] = pack8(pacc, 0);
+          stash(qb, 0, dsb[0]);
           bf16x8 ot = tr_read_pair(so + tr_off(0), so + tr_off(0) + 8 * LD);
           bf16x8 qt_ = tr_read_pair(sq + tr_off(0), sq + tr_off(0) + 8 * LD);
           __builtin_amdgcn_sched_barrier(0);
@@ -680,6 +744,7 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
           }
           pb[1] = pack8(sacc, 8);
           dsb[1] = pack8(pacc, 8);
+          stash(qb, 1, dsb[1]);
 #pragma unroll
           for (int i = NDB; i < 2 * NDB; ++i) {
             dvacc[i - NDB] = mfma32(ot, pb[1], dvacc[i - NDB]);
@@ -738,6 +803,7 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
           else
             grads(std::false_type{});
           const bf16x8 pb = pack8(sacc, 8 * t), dsb = pack8(pacc, 8 * t);
+          stash(qb, t, dsb);
           __builtin_amdgcn_sched_barrier(0);
           bf16x8 ot[NDB], qt_[NDB];
 #pragma unroll
@@ -825,6 +891,7 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
       auto pack = [&](int qb, int t) {
         pb[qb][t] = pack8(sacc[qb], 8 * t);
         dsb[qb][t] = pack8(pacc[qb], 8 * t);
+        stash(qb, t, dsb[qb][t]);
       };
       // dV / dK products of quarter (qb, t), step db carrying gradient elements
       // [g0 + 8 db / NDB, g0 + 8 (db + 1) / NDB) of block gq (none when gq < 0).
@@ -985,6 +1052,8 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
       pb[0][1] = pack8(sacc[0], 8);
       dsb[0][0] = pack8(pacc[0], 0);
       dsb[0][1] = pack8(pacc[0], 8);
+      stash(0, 0, dsb[0][0]);
+      stash(0, 1, dsb[0][1]);
       bf16x8 ot[2], qt_[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -1000,6 +1069,8 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
           pb[1][1] = pack8(sacc[1], 8);
           dsb[1][0] = pack8(pacc[1], 0);
           dsb[1][1] = pack8(pacc[1], 8);
+          stash(1, 0, dsb[1][0]);
+          stash(1, 1, dsb[1][1]);
         }
         dvacc[db] = mfma32(ot[i & 1], pb[qb][t], dvacc[db]);
         dkacc[db] = mfma32(qt_[i & 1], dsb[qb][t], dkacc[db]);
@@ -1031,6 +1102,20 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
       step_split(it, sq, so, sl, sd, sm);
   };
 
+  // The fragments of iteration it's dS, stored after the barrier that ends the iteration: the
+  // wait before that barrier counts stores too, so stores issued inside the step would hold it
+  // for a write round trip; issued here they overlap the next iteration's work.  A wave whose
+  // step skipped the tile has nothing to store.
+  auto export_after = [&](int it) __attribute__((always_inline)) {
+    const int hh = it / nq;
+    const int q0 = q_tile(it, hh);
+    const int q_last = min(q0 + kBMt - 1, T - 1);
+    const bool skip = !wave_active || q_last < kw0 || q0 > e_hi ||
+                      (window > 0 && q0 > kw_last + window - 1);
+    if constexpr (EXPORT)
+      if (!skip) export_ds(hh, q0);
+  };
+
   // Two-deep pipeline over the (query head, query tile) iterations, unrolled by two so each
   // LDS buffer is a distinct array: the loads into one buffer never wait on reads of the other.
   dma(0, 0);
@@ -1041,11 +1126,13 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
     step(it, sQ0, sO0, sL[0], sD[0], sM0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    export_after(it);
     if (it + 1 >= nit) break;
     if (it + 2 < nit) dma(it + 2, 0);
     step(it + 1, sQ1, sO1, sL[1], sD[1], sM1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    export_after(it + 1);
   }
 
   finish_grad_row<D>(dkacc, a.scale, a.k + krowoff, a.dk + krowoff, krow, gl, a.pro != 0, a.rp,
@@ -1061,6 +1148,112 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
         store4(a.dv + krowoff + 32 * db + 8 * i4 + 4 * gl, v4);
       }
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ from exported dS (split backward)
+// ------------------------------------------------------------------------------------------
+// One workgroup per (b, h, 128 queries), 4 waves x 32 queries, the dq pass's grid order.  Per
+// 64-key tile: k^ staged in LDS (double buffered), the wave's four dS fragments (16 keys each)
+// loaded straight into MFMA B operands, and dQ^T += K^T dS^T with K^T read transposed from
+// LDS.  The fragments of the next tile are in flight while the current one multiplies.  No
+// score, exponential or dP is recomputed; the epilogue is the dq pass's (scale, RMSNorm and
+// RoPE backward).
+template <int D>
+__global__ __launch_bounds__(256, D <= 96 ? 4 : 3) void bwd_dq_ds_kernel(BwdArgs a) {
+  constexpr int LD = D + 8;
+  constexpr int NDB = D / 32;
+  constexpr int TILE = kBNk * LD;
+  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
+
+  const int T = a.T;
+  const int nbh = a.B * a.Hq;
+  const int rank = blockIdx.x / nbh;
+  const int bh = xcd_local_head(blockIdx.x - rank * nbh, nbh);
+  const int qt = a.ntiles - 1 - rank;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int g = h / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x, l = tid & 63, gl = l >> 5, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q0 = qt * kBMq, qw0 = q0 + 32 * w;
+  const int qi = qw0 + lr;
+  const int qrow = min(qi, T - 1);
+  const bf16* kbase = a.kh + (int64_t)(b * a.Hkv + g) * T * D;
+  const int64_t rowoff = ((int64_t)bh * T + qrow) * D;
+  const bool wave_active = qw0 < T;
+  // This wave's 32-query block and its key blocks.
+  const int iq = qw0 >> 5;
+  const int jlo = ds_lo(iq, a.band), jhi = ds_hi(iq, a.band);
+  const bf16* dsh = a.ds + ((int64_t)bh * a.band.frags) * 512 + 8 * l;
+
+  const int window = a.window;
+  const int k_end = min(T, q0 + kBMq);
+  const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
+  const int kt0 = k_begin / kBNk, kt1 = (k_end - 1) / kBNk;
+
+  const TileDma<D, 4> tdma(w, l);
+  // Fragment f of tile kt (key block 4 kt + f), or zeros outside this wave's band.
+  auto frag_in = [&](int kt, int f) {
+    const int j = 4 * kt + f;
+    return wave_active && j >= jlo && j <= jhi;
+  };
+  auto load_frags = [&](bf16x8 (&fr)[4], int kt) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (frag_in(kt, f))
+        fr[f] = __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x8*>(dsh + ds_frag(iq, 4 * kt + f, a.band) * 512));
+    }
+  };
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  // K^T operand of key block f, head-dim block db: lane (group gq, L) loads key row
+  // 16 f + 8 (gq / 2) + L / 4 (+ 4) at columns 32 db + 16 (gq % 2) + 4 (L % 4).
+  const int gq = l >> 4, L = l & 15;
+  const int aoff = (8 * (gq >> 1) + (L >> 2)) * LD + 16 * (gq & 1) + 4 * (L & 3);
+  auto run = [&](int kt, const bf16* sk, const bf16x8 (&fr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (!frag_in(kt, f)) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16* p0 = sk + 16 * f * LD + 32 * db + aoff;
+        dqacc[db] = mfma32(tr_read_pair(p0, p0 + 4 * LD), fr[f], dqacc[db]);
+      }
+    }
+  };
+
+  bf16x8 fr0[4], fr1[4];
+  tdma.copy(sK0, kbase, kt0 * kBNk, T, w);
+  load_frags(fr0, kt0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; kt += 2) {
+    if (kt + 1 <= kt1) {
+      tdma.copy(sK1, kbase, (kt + 1) * kBNk, T, w);
+      load_frags(fr1, kt + 1);
+    }
+    run(kt, sK0, fr0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 > kt1) break;
+    if (kt + 2 <= kt1) {
+      tdma.copy(sK0, kbase, (kt + 2) * kBNk, T, w);
+      load_frags(fr0, kt + 2);
+    }
+    run(kt + 1, sK1, fr1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  finish_grad_row<D>(dqacc, a.scale, a.q + rowoff, a.dq + rowoff, qrow, gl, a.pro != 0, a.rp,
+                     qi < T);
 }
 
 BwdArgs make_args(const BwdParams& p, int D) {
@@ -1094,7 +1287,21 @@ BwdArgs make_args(const BwdParams& p, int D) {
   a.scale = p.scale;
   a.sc = make_score_setup(p.scale, p.softcap, D, p.qk_norm).coef;
   a.rp = make_row_prologue(p.rope, p.rope_base, p.qk_norm, p.eps, D);
+  a.ds = (bf16*)p.ds;
+  a.band = p.band;
   return a;
+}
+
+template <int D>
+hipError_t launch_dq_ds_d(const BwdParams& p, hipStream_t s) {
+  BwdArgs a = make_args(p, D);
+  a.ntiles = (p.T + kBMq - 1) / kBMq;
+  const dim3 grid((unsigned)(a.ntiles * p.B * p.Hq));
+  static const char* names[4] = {"bwd_dq_ds_d32", "bwd_dq_ds_d64", "bwd_dq_ds_d96",
+                                 "bwd_dq_ds_d128"};
+  TraceScope t(names[D / 32 - 1], s);
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<D>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -1127,6 +1334,18 @@ hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool DROP, bool EXPORT>
+void launch_dkdv_mode(const BwdArgs& a, int mode, dim3 grid, hipStream_t s) {
+  if (mode == kScoreScale)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale, DROP, EXPORT>), grid, dim3(256), 0, s, a);
+  else if (mode == kScoreCapPoly5)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5, DROP, EXPORT>), grid, dim3(256), 0, s, a);
+  else if (mode == kScoreCapPoly)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly, DROP, EXPORT>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp, DROP, EXPORT>), grid, dim3(256), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_dkdv_d(const BwdParams& p, hipStream_t s) {
   BwdArgs a = make_args(p, D);
@@ -1134,26 +1353,15 @@ hipError_t launch_dkdv_d(const BwdParams& p, hipStream_t s) {
   const int mode = make_score_setup(p.scale, p.softcap, D, p.qk_norm).mode;
   const dim3 grid((unsigned)(a.ntiles * p.B * p.Hkv));
   static const char* names[4] = {"bwd_dkdv_d32", "bwd_dkdv_d64", "bwd_dkdv_d96", "bwd_dkdv_d128"};
-  TraceScope t(names[D / 32 - 1], s);
-  if (a.drop_cols) {
-    if (mode == kScoreScale)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale, true>), grid, dim3(256), 0, s, a);
-    else if (mode == kScoreCapPoly5)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5, true>), grid, dim3(256), 0, s, a);
-    else if (mode == kScoreCapPoly)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly, true>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp, true>), grid, dim3(256), 0, s, a);
-  } else {
-    if (mode == kScoreScale)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreScale, false>), grid, dim3(256), 0, s, a);
-    else if (mode == kScoreCapPoly5)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly5, false>), grid, dim3(256), 0, s, a);
-    else if (mode == kScoreCapPoly)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapPoly, false>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kScoreCapExp, false>), grid, dim3(256), 0, s, a);
-  }
+  static const char* xnames[4] = {"bwd_dkdv_export_d32", "bwd_dkdv_export_d64",
+                                  "bwd_dkdv_export_d96", "bwd_dkdv_export_d128"};
+  TraceScope t((a.ds ? xnames : names)[D / 32 - 1], s);
+  if (a.drop_cols)
+    launch_dkdv_mode<D, true, false>(a, mode, grid, s);
+  else if (a.ds)
+    launch_dkdv_mode<D, false, true>(a, mode, grid, s);
+  else
+    launch_dkdv_mode<D, false, false>(a, mode, grid, s);
   return hipGetLastError();
 }
 
@@ -1165,6 +1373,16 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     case 64: return launch_dq_d<64>(p, s);
     case 96: return launch_dq_d<96>(p, s);
     case 128: return launch_dq_d<128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_ds(const BwdParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_dq_ds_d<32>(p, s);
+    case 64: return launch_dq_ds_d<64>(p, s);
+    case 96: return launch_dq_ds_d<96>(p, s);
+    case 128: return launch_dq_ds_d<128>(p, s);
   }
   return hipErrorInvalidValue;
 }

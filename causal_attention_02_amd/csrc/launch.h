@@ -95,6 +95,11 @@ hipError_t launch_append_kv(const void* kn, const void* vn, void* kc, void* vc,
                             float eps, hipStream_t s);
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s);
+// Backward preparation over the [B, Hq, T] query rows: nD = -rowsum(dO * O), L2 = LSE * log2(e)
+// and, when qh is not null, qh = N(R(q)) (bf16).
+hipError_t launch_bwd_prep(const void* q, const void* o, const void* dO, const float* lse,
+                           void* qh, float* nD, float* L2, int64_t rows, int T, int D, int rope,
+                           float rope_base, int qk_norm, float eps, hipStream_t s);
 
 // ---- attention dropout (dropout.hip) ------------------------------------------------------
 // Keep masks, one bit per (query, key): 32-bit words, `dropout_pitch(T)` words per row (an even
@@ -135,6 +140,41 @@ struct FwdParams {
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);  // q, k already prologued
 
+// ---- dS fragments (split backward) ----------------------------------------------------------
+// The dK/dV pass stores dS (bf16) of every (32-query block i, 16-key block j) that holds a
+// visible pair as one 1 KB fragment: 64 lanes x 8 values in the B-operand layout of
+// v_mfma_f32_32x32x16_bf16 (lane l: query 32 i + l % 32, keys 16 j + 8 (l / 32) + 0..7).
+// Block i spans key blocks lo_i .. hi_i with hi_i = min(2 i + 1, nkb - 1) and lo_i =
+// floor(max(0, 32 i - W + 1) / 16) (0 without a window).  Without a window (or W >= T) the
+// fragments of a head are packed as a triangle, index i (i + 1) + j; with one, as a band of
+// `stride` fragments per block, index i stride + j - lo_i.
+struct DsBand {
+  int nqb, nkb;     // 32-query blocks, 16-key blocks
+  int window;       // W when 0 < W < T, else 0
+  int stride;       // 0: triangle; else fragments per query block
+  int64_t frags;    // fragments per (b, h)
+};
+inline DsBand make_ds_band(int T, int window) {
+  DsBand d{};
+  d.nqb = (T + 31) / 32;
+  d.nkb = (T + 15) / 16;
+  d.window = (window > 0 && window < T) ? window : 0;
+  if (d.window == 0) {
+    d.stride = 0;
+    d.frags = (int64_t)d.nqb * (d.nqb + 1);
+  } else {
+    int S = 1;
+    for (int i = 0; i < d.nqb; ++i) {
+      const int hi = 2 * i + 1 < d.nkb - 1 ? 2 * i + 1 : d.nkb - 1;
+      const int lo = (32 * i - d.window + 1 > 0 ? 32 * i - d.window + 1 : 0) / 16;
+      if (hi - lo + 1 > S) S = hi - lo + 1;
+    }
+    d.stride = S;
+    d.frags = (int64_t)d.nqb * S;
+  }
+  return d;
+}
+
 // ---- backward (bwd.hip) ------------------------------------------------------------------
 struct BwdParams {
   const void* q;     // raw q (bf16) [B, Hq, T, D]
@@ -163,9 +203,17 @@ struct BwdParams {
   const uint32_t* drop_rows = nullptr;
   const uint32_t* drop_cols = nullptr;
   float drop_scale = 1.f;
+  // Split backward: dS fragments [B * Hq, band.frags, 512] bf16 written by the dK/dV pass and
+  // read by launch_bwd_dq_ds (null: the dq pass recomputes dS instead).
+  void* ds = nullptr;
+  DsBand band{};
 };
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t s);
+// dQ from the dS fragments the dK/dV pass exported (p.ds): no recomputation of S or dP.
+hipError_t launch_bwd_dq_ds(const BwdParams& p, hipStream_t s);
+
+
 
 // ---- decode (decode.hip) -----------------------------------------------------------------
 // Query heads handled by one decode workgroup: the largest of 4, 3, 2, 1 that divides the

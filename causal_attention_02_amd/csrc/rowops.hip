@@ -249,6 +249,94 @@ hipError_t launch_segment_bounds(const int32_t* ids, int32_t* start, int32_t* en
   return hipGetLastError();
 }
 
+// Backward preparation, one pass over the query rows (same lane layout as
+// prologue_bf16_kernel: 8 lanes per row, each owning elements 8u..8u+7 of both halves):
+//   nD[r] = -sum_d dO[r, d] O[r, d]   (the softmax-gradient row term, negated)
+//   L2[r] = LSE[r] * log2(e)          (the backward works in log2 units)
+//   qh[r] = N(R(q[r]))                (when qh is not null: RoPE at position r % T, RMSNorm)
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ q,
+                                                       const bf16* __restrict__ o,
+                                                       const bf16* __restrict__ dO,
+                                                       const float* __restrict__ lse,
+                                                       bf16* __restrict__ qh, float* __restrict__ nD,
+                                                       float* __restrict__ L2, int64_t rows,
+                                                       int Tlen, int D, RowPrologue rp) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int u = threadIdx.x & 7;
+  const bool act = row < rows && u < D / 16;
+  const int half = D / 2;
+  const int64_t off = (row < rows ? row : 0) * D;
+  float dsum = 0.f;
+  if (act) {
+    const bf16x8 o1 = ld16<bf16x8>(o + off + 8 * u), o2 = ld16<bf16x8>(o + off + half + 8 * u);
+    const bf16x8 g1 = ld16<bf16x8>(dO + off + 8 * u), g2 = ld16<bf16x8>(dO + off + half + 8 * u);
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      dsum = fmaf((float)g1[p], (float)o1[p], fmaf((float)g2[p], (float)o2[p], dsum));
+  }
+  dsum += __shfl_xor(dsum, 1, 8);
+  dsum += __shfl_xor(dsum, 2, 8);
+  dsum += __shfl_xor(dsum, 4, 8);
+  if (row < rows && u == 0) {
+    nD[row] = -dsum;
+    L2[row] = lse[row] * kLog2e;
+  }
+  if (!qh) return;
+  float x1[8], x2[8];
+  if (act) {
+    const bf16x8 a = ld16<bf16x8>(q + off + 8 * u);
+    const bf16x8 c = ld16<bf16x8>(q + off + half + 8 * u);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      x1[p] = (float)a[p];
+      x2[p] = (float)c[p];
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) x1[p] = x2[p] = 0.f;
+  }
+  if (rp.rope && act) {
+    const int pos = (int)(row % Tlen);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) rope_pair(x1[p], x2[p], pos, rp.omega_rev[8 * u + p], false);
+  }
+  if (rp.qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) ss += x1[p] * x1[p] + x2[p] * x2[p];
+    ss += __shfl_xor(ss, 1, 8);
+    ss += __shfl_xor(ss, 2, 8);
+    ss += __shfl_xor(ss, 4, 8);
+    const float inv = 1.0f / sqrtf(ss / (float)D + rp.eps);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      x1[p] *= inv;
+      x2[p] *= inv;
+    }
+  }
+  if (act) {
+    bf16x8 a, c;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      a[p] = to_bf16(x1[p]);
+      c[p] = to_bf16(x2[p]);
+    }
+    *reinterpret_cast<bf16x8*>(qh + off + 8 * u) = a;
+    *reinterpret_cast<bf16x8*>(qh + off + half + 8 * u) = c;
+  }
+}
+
+hipError_t launch_bwd_prep(const void* q, const void* o, const void* dO, const float* lse,
+                           void* qh, float* nD, float* L2, int64_t rows, int T, int D, int rope,
+                           float rope_base, int qk_norm, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  TraceScope t("bwd_prep", s);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s,
+                     (const bf16*)q, (const bf16*)o, (const bf16*)dO, lse, (bf16*)qh, nD, L2, rows,
+                     T, D, make_row_prologue(rope, rope_base, qk_norm, eps, D));
+  return hipGetLastError();
+}
+
 hipError_t launch_prologue(const void* x, void* y, int64_t rows, int T, int D, int elt, int rope,
                            float rope_base, int qk_norm, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

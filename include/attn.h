@@ -102,7 +102,10 @@ typedef struct {
 } attn_extend_cfg;
 
 /* Bytes of device workspace that attn_fwd / attn_bwd / attn_decode need for this
- * configuration (0 if none).  Host-only; returns 0 for an invalid configuration. */
+ * configuration (0 if none).  Host-only; returns 0 for an invalid configuration.  The
+ * split backward's (attn_bwd_split_workspace_bytes) adds the dS fragments its dK/dV pass
+ * stores for the dQ pass: 1 KB per (32-query, 16-key) block in the causal / window band,
+ * e.g. 545 MB at B = 16, T = 2048, 8 query heads. */
 size_t attn_fwd_workspace_bytes(const attn_cfg* cfg);
 size_t attn_bwd_workspace_bytes(const attn_cfg* cfg);
 size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg);
@@ -110,6 +113,7 @@ size_t attn_decode_workspace_bytes(const attn_decode_cfg* cfg);
  * region 256-byte aligned). */
 size_t attn_fwd_packed_workspace_bytes(const attn_cfg* cfg);
 size_t attn_bwd_packed_workspace_bytes(const attn_cfg* cfg);
+size_t attn_bwd_split_workspace_bytes(const attn_cfg* cfg);
 
 /* Host-only validation of a configuration; the status attn_fwd would return for it
  * (before pointer and workspace checks).  for_backward = 1 applies the backward's rules. */
@@ -140,6 +144,20 @@ int attn_fwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, v
 int attn_bwd(const attn_cfg* cfg, const void* q, const void* k, const void* v, const void* o,
              const void* dO, const float* lse, void* dq, void* dk, void* dv, void* ws,
              size_t ws_bytes, void* stream);
+
+/*
+ * attn_bwd_split -- attn_bwd computed another way (same arguments, same results up to fp32
+ * rounding order, deterministic): the dK/dV pass also stores dS (bf16, the value the dQ product
+ * uses in attn_bwd as well) for every 32 x 16 (query, key) block of the mask's band, and dQ is
+ * then a product of those blocks with k^, instead of a pass that recomputes S, P and dP per
+ * query tile.  It moves about twice the backward's other HBM traffic through memory
+ * (545 MB written and read at B = 16, T = 2048, 8 query heads) and measured slower than
+ * attn_bwd on MI355X; it is kept as a checked alternative.  Workspace:
+ * attn_bwd_split_workspace_bytes(cfg).  Plain rows without dropout only.
+ */
+int attn_bwd_split(const attn_cfg* cfg, const void* q, const void* k, const void* v,
+                   const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * attn_bwd_khat -- attn_bwd without its own pass over k: khat is k after RoPE / QK-norm,

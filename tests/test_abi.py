@@ -71,6 +71,15 @@ def test_workspace_sizes(L):
     plain = cfg(B=16, T=2048, opts=bd.AttnOptions())
     assert L.attn_fwd_workspace_bytes(ctypes.byref(plain)) == 0
     assert L.attn_bwd_workspace_bytes(ctypes.byref(plain)) == 2 * rows * 4
+    # Split backward: the same regions, then the dS fragments: per (b, h) the triangle of 64
+    # 32-query blocks x their 16-key blocks, 64 * 65 fragments of 1 KB.
+    ds = 16 * 8 * 64 * 65 * 1024
+    assert L.attn_bwd_split_workspace_bytes(ctypes.byref(c)) == \
+        L.attn_bwd_workspace_bytes(ctypes.byref(c)) + ds
+    # A window of 512 keeps a band: blocks i >= 16 span 33 or 34 key blocks, stride 34.
+    win = cfg(B=16, T=2048, opts=bd.AttnOptions(window=512))
+    assert L.attn_bwd_split_workspace_bytes(ctypes.byref(win)) == \
+        L.attn_bwd_workspace_bytes(ctypes.byref(win)) + 16 * 8 * 64 * 34 * 1024
     assert L.attn_fwd_workspace_bytes(ctypes.byref(cfg(Hq=5))) == 0  # invalid -> 0
     # Decode: [tickets, one uint32 per (b, kv head, head subset)][partials B*Hq*nsplit*(D+2)
     # f32], each region 256-byte aligned.

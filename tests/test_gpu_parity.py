@@ -38,7 +38,7 @@ def oracle_kw(w: Workload) -> dict:
                 qk_norm=w.qk_norm, norm_eps=w.norm_eps)
 
 
-def gpu_fwd_bwd(w: Workload, q, k, v, dO):
+def gpu_fwd_bwd(w: Workload, q, k, v, dO, split=False):
     import torch
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     tq, tk, tv = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
@@ -46,7 +46,7 @@ def gpu_fwd_bwd(w: Workload, q, k, v, dO):
     grads = None
     if dO is not None:
         tdo = to_dev(dO, dt)
-        grads = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))
+        grads = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w), split=split)
     torch.cuda.synchronize()
     out = (to_host(o), to_host(lse))
     if grads is not None:
@@ -121,12 +121,13 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["bwd", "bwd_split"])
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
-def test_bf16_fwd_bwd_small(w):
-    _say(f"case {w.name}: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} W={w.window} "
-         f"cap={w.softcap} rope={w.rope} norm={w.qk_norm}")
+def test_bf16_fwd_bwd_small(w, split):
+    _say(f"case {w.name} split={split}: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+         f"W={w.window} cap={w.softcap} rope={w.rope} norm={w.qk_norm}")
     q, k, v, dO = make_train_inputs(w)
-    got = gpu_fwd_bwd(w, q, k, v, dO)
+    got = gpu_fwd_bwd(w, q, k, v, dO, split=split)
     ref_f = attention_forward(q, k, v, **oracle_kw(w))
     if w.T > 2:
         ref_b = attention_backward(q, k, v, dO, **oracle_kw(w))
@@ -216,6 +217,17 @@ def test_full_size_every_slice(name):
     check_every_slice(w, q, k, v, dO, got, name, lambda b: oracle_kw(w))
 
 
+@pytest.mark.parametrize("name", ["gqa181m_train", "flaxchat_w512"])
+def test_split_backward_full_size_every_slice(name):
+    """attn_bwd_split at full size (the triangle layout of the dS fragments, and the band layout
+    of a 512 window), every (b, KV-group) slice against the oracle."""
+    w = WORKLOADS[name]
+    _say(f"case {name} split backward full size: B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
+    q, k, v, dO = make_train_inputs(w)
+    got = gpu_fwd_bwd(w, q, k, v, dO, split=True)
+    check_every_slice(w, q, k, v, dO, got, name + "/split", lambda b: oracle_kw(w))
+
+
 def test_bwd_khat_equals_bwd():
     """attn_bwd with the forward's k^ (the start of its workspace) gives attn_bwd's gradients
     bitwise, for the RoPE/QK-norm workloads and for plain attention (khat unused)."""
@@ -237,14 +249,15 @@ def test_bwd_khat_equals_bwd():
             assert torch.equal(a, b), w.name
 
 
-def test_backward_is_deterministic():
+@pytest.mark.parametrize("split", [False, True], ids=["bwd", "bwd_split"])
+def test_backward_is_deterministic(split):
     import torch
     w = WORKLOADS["gqa181m_train"].with_(B=2, T=512)
     q, k, v, dO = make_train_inputs(w)
     tq, tk, tv, tdo = (to_dev(x, torch.bfloat16) for x in (q, k, v, dO))
     o, lse = attn_fwd(tq, tk, tv, opts_of(w))
-    g1 = [t.clone() for t in attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))]
-    g2 = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w))
+    g1 = [t.clone() for t in attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w), split=split)]
+    g2 = attn_bwd(tq, tk, tv, o, tdo, lse, opts_of(w), split=split)
     o2, lse2 = attn_fwd(tq, tk, tv, opts_of(w))
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
