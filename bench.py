@@ -33,25 +33,32 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal attn fwd+bwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s"
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bwd_dkdv_gqa181m_train.md")
-KERNEL_SOURCES = ["bwd.hip", "device_common.h", "launch.h"]
+# Counter summaries (FETCH_SIZE / WRITE_SIZE runs, calibrated on a plain copy) and the sources
+# whose hash each one is valid for.
+TRAFFIC_FILES = {
+    "bwd_dkdv_d96": ("hbm_traffic_bwd_dkdv_gqa181m_train.md", ["bwd.hip", "device_common.h", "launch.h"]),
+    "decode_split_d96": ("hbm_traffic_decode_gqa181m_decode.md",
+                         ["decode.hip", "device_common.h", "launch.h"]),
+}
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(names):
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "causal_attention_02_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
-    WRITE_SIZE runs, calibrated on a plain copy), or None when there is none for this kernel
-    or its sources changed since the counters were taken."""
+    """HBM bytes per launch of `kernel` from its committed counter summary, or None when there
+    is none for this kernel or its sources changed since the counters were taken."""
+    if kernel not in TRAFFIC_FILES:
+        return None
+    fname, sources = TRAFFIC_FILES[kernel]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", fname)) as f:
             for line in f:
                 if line.startswith("bench-traffic:"):
                     rec = json.loads(line.split(":", 1)[1])
@@ -60,9 +67,9 @@ def measured_traffic(kernel):
                 return None
     except OSError:
         return None
-    if rec.get("kernel") != kernel or rec.get("sources_sha256") != kernel_sources_sha256():
+    if rec.get("kernel") != kernel or rec.get("sources_sha256") != kernel_sources_sha256(sources):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_launch", rec.get("bytes_per_call"))
 
 
 def visible_tiles32(T, window):
@@ -91,6 +98,12 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) so HBM byte "
                          "counters can be calibrated against a known size")
+    ap.add_argument("--profile-workload", default=None,
+                    help="run only this workload's step (a training workload's fwd+bwd, or a "
+                         "decode workload's call) --steps times after --warmup, for a profiler; "
+                         "prints one line and skips everything else")
+    ap.add_argument("--profile-split", action="store_true",
+                    help="with --profile-workload: time attn_bwd_split instead of attn_bwd")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path has no "
@@ -123,6 +136,18 @@ def main():
     def opts_of(w):
         return bd.AttnOptions(window=w.window, softcap=w.softcap, rope=w.rope,
                               rope_base=w.rope_base, qk_norm=w.qk_norm, norm_eps=w.norm_eps)
+
+    def calibration_copy():
+        nb = args.copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {args.copy_mib} MiB device-to-device")
+        del src, dst
+        torch.cuda.empty_cache()
 
     def to_dev(x):
         return torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
@@ -221,6 +246,38 @@ def main():
             kern = bd.trace_read()
             bd.trace_enable(False)
         return total_ms / steps, per, kern
+
+    if args.profile_workload:
+        # One workload only, for a profiler: a training step (fwd + bwd) or a decode call over
+        # --decode-copies cache copies.
+        w = WORKLOADS[args.profile_workload]
+        if args.copy_mib > 0:
+            calibration_copy()
+        if w.decode:
+            qd, kc, vc, lens = make_decode_inputs(w)
+            tq = to_dev(qd)
+            tk0, tv0 = to_dev(kc), to_dev(vc)
+            del kc, vc
+            cps = [(tk0, tv0)] + [(tk0.clone(), tv0.clone()) for _ in range(args.decode_copies - 1)]
+            tl = torch.from_numpy(lens).to(dev)
+            od = torch.empty_like(tq)
+            wsp = bd.decode_workspace(w.B, w.Hq, w.Hkv, w.D, w.T, opts_of(w))
+
+            def one(i):
+                kk, vv = cps[i % len(cps)]
+                bd.attn_decode(tq, kk, vv, tl, opts_of(w), out=od, workspace=wsp)
+
+            for i in range(args.warmup):
+                one(i)
+            ms = timed(one, args.steps) / args.steps
+            log(f"[bench] profile {w.name}: {ms * 1e3:.1f} us/call over {args.steps} calls, "
+                f"{decode_bytes(w, lens) / 1e6:.1f} MB of active K/V per call")
+        else:
+            ids = make_segment_ids(w) if w.seg_lo > 0 else None
+            ms, _, _ = train_case(w, args.steps, args.warmup, ids=ids, split=args.profile_split)
+            log(f"[bench] profile {w.name}: {ms:.3f} ms/step over {args.steps} steps")
+        print(json.dumps({"profile_workload": w.name, "ms": ms, "steps": args.steps}), flush=True)
+        return
 
     result = {}
     extra = {}
@@ -322,16 +379,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.copy_mib > 0:
-        nb = args.copy_mib << 20
-        src = torch.empty(nb, dtype=torch.uint8, device=dev)
-        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-        src.fill_(1)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy: 3 x {args.copy_mib} MiB device-to-device")
-        del src, dst
-        torch.cuda.empty_cache()
+        calibration_copy()
 
     # ------------------------------------------------------------------------------------
     # decode
@@ -374,6 +422,7 @@ def main():
         extra["decode"] = dict(ms_per_call=ms_d, marker_ms_median=float(np.median(per)),
                                marker_ms_p90=float(np.percentile(per, 90)), GBps=gbs,
                                pct_hbm_peak=100 * gbs / PEAK_HBM_GBS, bytes_per_call=nbytes,
+                               measured_hbm_bytes_per_call=measured_traffic("decode_split_d96"),
                                kernels_ms=split)
         log(f"[bench] decode: {ms_d * 1e3:.1f} us/call  {gbs:.0f} GB/s")
         # The GPT pretraining page's KV-cache shape (one sequence, 256 cached rows, 12 heads,
