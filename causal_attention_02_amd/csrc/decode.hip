@@ -91,6 +91,12 @@ __device__ __forceinline__ void merge_state(RunState<NE>& s, float mp, float lp,
   s.m = mn;
 }
 
+// A DPP lane permutation of x (CTRL: the dpp_ctrl encoding).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 // Rotation by 4 or 8 lanes inside each row of 16 (DPP row_ror:4 / row_ror:8).
 template <int R>
 __device__ __forceinline__ float dpp_ror(float x) {
@@ -156,6 +162,7 @@ struct RowMap {
   typedef __bf16 G __attribute__((ext_vector_type(EPG)));
   static __device__ __forceinline__ int dim(int j, int k, int e) { return (j + LPR * k) * EPG + e; }
   static_assert(LPR * NG * EPG == D, "the LPR lanes' granules tile the row exactly");
+  static_assert(LPR == 4 || LPR == 8, "the score sums cover quads or half rows of lanes");
 };
 
 // Workgroups resident per CU: two with four lanes per row; with eight, four (three when the
@@ -239,17 +246,43 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
   struct Buf {
     Gv k[NSTEP][NG], v[NSTEP][NG];
   };
+  // The loads address a uniform base (scalar registers) plus one 32-bit byte offset per lane
+  // and step (below Lmax * 2D <= 2^32, checked on the host), with the granule's position as an
+  // immediate.  The offsets of the next pass are computed as soon as the previous pass has been
+  // issued, so they sit in registers of their own: an address register that had been a load
+  // target would make the next pass wait for the loads still in flight.
+  auto uniform = [](const bf16* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const __attribute__((address_space(1))) char*)(((uint64_t)hi << 32) | lo);
+  };
+  const auto kbase = uniform(kb);
+  const auto vbase = uniform(vb);
+  const uint32_t lane_byte = 2u * (uint32_t)RM::dim(j8, 0, 0);
+  auto offsets = [&](uint32_t (&o)[NSTEP], int pass) {
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      o[st] = (uint32_t)min(row0 + kPass * pass + kRowsPerStep * st, stop - 1) * (uint32_t)(2 * D) +
+              lane_byte;
+      asm volatile("" : "+v"(o[st]));
+    }
+  };
+  uint32_t onext[NSTEP];
+  offsets(onext, 0);
+  // Passes are loaded in order 0, 1, 2, ...; each call issues the pass `onext` points at.
   auto load = [&](Buf& bu, int pass) {
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      const int64_t off = (int64_t)min(row0 + kPass * pass + kRowsPerStep * st, stop - 1) * D;
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
         // Granule u of this lane: elements RM::dim(j8, u, 0) .. + EPG - 1 of the row (< D).
-        bu.k[st][u] = *reinterpret_cast<const Gv*>(kb + off + RM::dim(j8, u, 0));
-        bu.v[st][u] = *reinterpret_cast<const Gv*>(vb + off + RM::dim(j8, u, 0));
+        const int gb = 2 * RM::dim(0, u, 0);  // bytes past the lane's first granule
+        bu.k[st][u] = *(const __attribute__((address_space(1))) Gv*)(kbase + onext[st] + gb);
+        bu.v[st][u] = *(const __attribute__((address_space(1))) Gv*)(vbase + onext[st] + gb);
       }
     }
+    offsets(onext, pass + 1);
   };
 
   Buf b0, b1;
@@ -310,8 +343,11 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
             const bf16x2 kp = {bu.k[stp][u][2 * e], bu.k[stp][u][2 * e + 1]};
             dot = __builtin_amdgcn_fdot2_f32_bf16(qv[hh][u * EPG / 2 + e], kp, dot, false);
           }
-#pragma unroll
-        for (int x = 1; x < LPR; x <<= 1) dot += __shfl_xor(dot, x, 64);
+        // Sum over the LPR lanes of the row: DPP quad permutations (xor 1, xor 2), then, for
+        // eight lanes, the mirror inside each half row of 8.
+        dot += dpp_f<0xB1>(dot);
+        dot += dpp_f<0x4E>(dot);
+        if constexpr (LPR == 8) dot += dpp_f<0x141>(dot);
         const float yy = score_y<MODE, false>(dot, a.sc, 0.f, nullptr);
         yv[stp][hh] = valid ? yy : kNegBig;
       }

@@ -411,7 +411,13 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
   }
 }
 
-// ---- fp32 forward: one thread per query, exact two-pass softmax in fp32 -----------------
+// ---- fp32 forward: 16 lanes per query, exact online softmax in fp32 ----------------------
+// A workgroup takes 16 consecutive queries of one (b, h); the 16 lanes of a query split its
+// visible keys (lane t takes keys k0 + t, k0 + t + 16, ...), each keeping a running (max,
+// sum, output row) with exact expf, and the 16 states are merged across the lanes at the end
+// (LSE-weighted).  The dot products run in four independent partial sums, so the latency of
+// one fused multiply-add chain does not set the pace.  This is the fp32 parity path of small
+// shapes; the bf16 kernels above carry the large workloads.
 struct FwdF32Args {
   const float* q;
   const float* k;
@@ -422,77 +428,95 @@ struct FwdF32Args {
   float scale, softcap;
 };
 
+constexpr int kF32Queries = 16;  // queries per workgroup (16 lanes each: 256 threads)
+
 template <int D>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
-  constexpr int BK = 32;
-  __shared__ float sK[BK][D];
-  __shared__ float sV[BK][D];
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Args a) {
+  static_assert(D % 4 == 0, "rows are read as float4");
   const int T = a.T;
   const int nbh = a.B * a.Hq;
   const int rank = blockIdx.x / nbh;
   const int bh = blockIdx.x - rank * nbh;
-  const int qt = a.nqt - 1 - rank;
+  const int qt = a.nqt - 1 - rank;  // heaviest query tiles first
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
-  const int tid = threadIdx.x;
-  const int q0 = qt * 64, qi = q0 + tid;
-  const int window = a.window;
+  const int r = threadIdx.x >> 4, t = threadIdx.x & 15;
+  const int q0 = qt * kF32Queries, qi = q0 + r;
+  const int qrow = min(qi, T - 1);
   const float* kb = a.k + (int64_t)(b * a.Hkv + g) * T * D;
   const float* vb = a.v + (int64_t)(b * a.Hkv + g) * T * D;
   float qv[D];
   {
-    const float* qp = a.q + ((int64_t)bh * T + min(qi, T - 1)) * D;
+    const float4* qp = reinterpret_cast<const float4*>(a.q + ((int64_t)bh * T + qrow) * D);
 #pragma unroll
-    for (int d = 0; d < D; ++d) qv[d] = qp[d];
-  }
-  const int k_end = min(T, q0 + 64);
-  const int k_begin = window > 0 ? max(0, q0 - window + 1) : 0;
-  auto visible = [&](int key) { return key <= qi && (window <= 0 || qi - key < window); };
-  auto score = [&](int j) {
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; ++d) s = fmaf(qv[d], sK[j][d], s);
-    s *= a.scale;
-    if (a.softcap > 0.f) s = a.softcap * tanhf(s / a.softcap);
-    return s;
-  };
-  float m = -INFINITY;
-  for (int k0 = (k_begin / BK) * BK; k0 < k_end; k0 += BK) {
-    for (int e = tid; e < BK * D; e += 64) {
-      const int key = k0 + e / D;
-      sK[e / D][e % D] = key < T ? kb[(int64_t)k0 * D + e] : 0.f;
+    for (int c = 0; c < D / 4; ++c) {
+      const float4 x = qp[c];
+      qv[4 * c] = x.x;
+      qv[4 * c + 1] = x.y;
+      qv[4 * c + 2] = x.z;
+      qv[4 * c + 3] = x.w;
     }
-    __syncthreads();
-    for (int j = 0; j < BK; ++j)
-      if (visible(k0 + j)) m = fmaxf(m, score(j));
-    __syncthreads();
   }
-  float lsum = 0.f;
+  // Keys [lo, qrow] are visible (lo from the window), as in the oracle's mask.
+  const int lo = a.window > 0 ? max(0, qrow - a.window + 1) : 0;
+  float m = -INFINITY, l = 0.f;
   float ov[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) ov[d] = 0.f;
-  for (int k0 = (k_begin / BK) * BK; k0 < k_end; k0 += BK) {
-    for (int e = tid; e < BK * D; e += 64) {
-      const int key = k0 + e / D;
-      sK[e / D][e % D] = key < T ? kb[(int64_t)k0 * D + e] : 0.f;
-      sV[e / D][e % D] = key < T ? vb[(int64_t)k0 * D + e] : 0.f;
+  for (int j = lo + t; j <= qrow; j += 16) {
+    const float4* kp = reinterpret_cast<const float4*>(kb + (int64_t)j * D);
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const float4 x = kp[c];
+      float& acc = part[c & 3];
+      acc = fmaf(qv[4 * c], x.x, acc);
+      acc = fmaf(qv[4 * c + 1], x.y, acc);
+      acc = fmaf(qv[4 * c + 2], x.z, acc);
+      acc = fmaf(qv[4 * c + 3], x.w, acc);
     }
-    __syncthreads();
-    for (int j = 0; j < BK; ++j)
-      if (visible(k0 + j)) {
-        const float p = expf(score(j) - m);
-        lsum += p;
+    float s = ((part[0] + part[1]) + (part[2] + part[3])) * a.scale;
+    if (a.softcap > 0.f) s = a.softcap * tanhf(s / a.softcap);
+    if (s > m) {
+      const float alpha = expf(m - s);  // 0 for the first key (m = -inf)
+      l *= alpha;
 #pragma unroll
-        for (int d = 0; d < D; ++d) ov[d] = fmaf(p, sV[j][d], ov[d]);
-      }
-    __syncthreads();
+      for (int d = 0; d < D; ++d) ov[d] *= alpha;
+      m = s;
+    }
+    const float p = expf(s - m);
+    l += p;
+    const float4* vp = reinterpret_cast<const float4*>(vb + (int64_t)j * D);
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const float4 x = vp[c];
+      ov[4 * c] = fmaf(p, x.x, ov[4 * c]);
+      ov[4 * c + 1] = fmaf(p, x.y, ov[4 * c + 1]);
+      ov[4 * c + 2] = fmaf(p, x.z, ov[4 * c + 2]);
+      ov[4 * c + 3] = fmaf(p, x.w, ov[4 * c + 3]);
+    }
   }
-  if (qi < T) {
-    float* op = a.o + ((int64_t)bh * T + qi) * D;
-    const float inv = 1.f / lsum;
+  // Merge the 16 lanes of the query: M = max m, l = sum l_t e^(m_t - M), o likewise.  A lane
+  // without keys holds m = -inf and l = 0 and contributes nothing.
 #pragma unroll
-    for (int d = 0; d < D; ++d) op[d] = ov[d] * inv;
-    a.lse[(int64_t)bh * T + qi] = m + logf(lsum);
+  for (int x = 1; x < 16; x <<= 1) {
+    const float m2 = __shfl_xor(m, x, 64);
+    const float l2 = __shfl_xor(l, x, 64);
+    const float mn = fmaxf(m, m2);
+    const float fa = m == -INFINITY ? 0.f : expf(m - mn);
+    const float fb = m2 == -INFINITY ? 0.f : expf(m2 - mn);
+    l = l * fa + l2 * fb;
+#pragma unroll
+    for (int d = 0; d < D; ++d) ov[d] = ov[d] * fa + __shfl_xor(ov[d], x, 64) * fb;
+    m = mn;
+  }
+  if (qi < T && t == 0) {
+    float4* op = reinterpret_cast<float4*>(a.o + ((int64_t)bh * T + qi) * D);
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c)
+      op[c] = make_float4(ov[4 * c] * inv, ov[4 * c + 1] * inv, ov[4 * c + 2] * inv, ov[4 * c + 3] * inv);
+    a.lse[(int64_t)bh * T + qi] = m + logf(l);
   }
 }
 
@@ -561,11 +585,11 @@ hipError_t launch_fwd_f32_d(const FwdParams& p, hipStream_t s) {
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.window = p.window;
-  a.nqt = (p.T + 63) / 64;
+  a.nqt = (p.T + kF32Queries - 1) / kF32Queries;
   a.scale = p.scale;
   a.softcap = p.softcap;
   TraceScope t("fwd_f32", s);
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)(a.nqt * p.B * p.Hq)), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)(a.nqt * p.B * p.Hq)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
