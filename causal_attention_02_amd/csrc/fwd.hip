@@ -220,8 +220,12 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
         // blocks in steps fenced by scheduling barriers: block 1's score MFMAs each followed
         // by a share of block 0's weights, then block 0's PV MFMAs each followed by a share
         // of block 1's weights.  LDS operands are read two steps ahead of their MFMA.
-        auto body = [&](auto masked) {
-          constexpr bool MASKED = decltype(masked)::value;
+        // One body for masked and unmasked tiles: an edge tile's invisible scores are replaced
+        // in place by kNegBig right after their MFMAs (a uniform branch around the selects),
+        // which the score transforms of this path send to -inf.  Two separate bodies would
+        // join with the output accumulators in different registers, and the copies that
+        // reconcile them cost more than the selects.
+        auto body = [&]() {
           // Steps an LDS operand read runs ahead of its MFMA (V: one at three waves per SIMD).
           constexpr int KPF = 2, VPF = (D <= 96 && VAR == kVarPlain) ? 1 : 2;
           // Three waves per SIMD leave no register to spare: there the fences hold only the
@@ -229,10 +233,15 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
           // still held to their step by the asm pins), which lets the allocator fit.
           constexpr int kFence = (D <= 96 && VAR == kVarPlain) ? 0x6 : 0;
           f32x16 sacc[2];
+          auto mask_block = [&](int kb) {
+            if (need_mask) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                sacc[kb][r] = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? sacc[kb][r] : kNegBig;
+            }
+          };
           auto weight = [&](int kb, int r) {
-            float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
-            if constexpr (MASKED)
-              y = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? y : kNegBig;
+            const float y = score_y<MODE, false>(sacc[kb][r], a.sc, m_run, nullptr);
             sacc[kb][r] = exp2_fast(y);
             // Pins the element's arithmetic to the step that asks for it.
             asm volatile("" : "+v"(sacc[kb][r]));
@@ -261,6 +270,7 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
 #pragma unroll
           for (int j = 0; j < 2 * NS; ++j) {
             const int kb = j / NS, s = j % NS;
+            if (j == NS) mask_block(0);
             sacc[kb] = mfma32(kr[j % KPF], bq[s], sacc[kb]);
             if (j + KPF < 2 * NS)
               kr[j % KPF] = ld16<bf16x8>(k_ptr((j + KPF) / NS, (j + KPF) % NS));
@@ -274,6 +284,7 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
           // product i % (2 NDB) = NDB t + db).  Block 1's weights share them out by halves:
           // elements 0-7 beside block 0's products, 8-15 beside block 1's first-half
           // products, which need only elements 0-7.
+          mask_block(1);
           bf16x8 pb[2][2];
           pack(0, 0, pb[0][0]);
           pack(0, 1, pb[0][1]);
@@ -302,10 +313,7 @@ __global__ __launch_bounds__(256, (D <= 96 && VAR == kVarPlain) ? 3 : 2) void fw
             __builtin_amdgcn_sched_barrier(kFence);
           }
         };
-        if (need_mask)
-          body(std::true_type{});
-        else
-          body(std::false_type{});
+        body();
       } else {
         f32x16 sacc[2];
 #pragma unroll
