@@ -251,9 +251,25 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
     // qi - key for element (kb, r) is qd - (32 kb + 8 (r / 4) + r % 4).
     const int qd = qi - k0 - 4 * gl;
 
+    // Score modes other than the exp form mask in place of the raw score (a.sc.mask_acc, right
+    // after a block's score MFMAs, in a uniform branch), so masked and unmasked tiles share one
+    // body: two bodies would join with the dQ accumulators in different registers, and the
+    // moves that reconcile them cost more than the selects.  The exp form's capped scores are
+    // bounded, so it keeps a masked body that masks after the transform.
+    constexpr bool kAccMask = MODE != kScoreCapExp;
     auto body = [&](auto masked) {
       f32x16 sacc[2], pacc[2];
       bf16x8 dsb[2][2];
+      auto mask_block = [&](int kb) {
+        if constexpr (kAccMask) {
+          if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sacc[kb][r] = visible(qd - (32 * kb + 8 * (r >> 2) + (r & 3)), lim) ? sacc[kb][r]
+                                                                                   : a.sc.mask_acc;
+          }
+        }
+      };
       // dS for element r of block kb, in place of its score.
       auto grad = [&](int kb, int r) {
         float gf;
@@ -295,6 +311,7 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
 #pragma unroll
       for (int j = 0; j < 2 * NS; ++j) {
         const int kb = j / NS, s = j % NS;
+        if (j == NS) mask_block(0);
         sacc[kb] = mfma32(ka[j % PF], bq[s], sacc[kb]);
         pacc[kb] = mfma32(va[j % PF], bdo[s], pacc[kb]);
         if (j + PF < 2 * NS) {
@@ -307,6 +324,7 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      mask_block(1);
       dsb[0][0] = pack8(sacc[0], 0);
       dsb[0][1] = pack8(sacc[0], 8);
       // Both blocks' dQ products as one stream of 4 NDB steps (step i: block i / (2 NDB),
@@ -338,7 +356,9 @@ __global__ __launch_bounds__(256, (D <= 96 || MODE == kScoreScale) ? 2 : 1) void
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (need_mask)
+    if constexpr (kAccMask)
+      body(std::false_type{});
+    else if (need_mask)
       body(std::true_type{});
     else
       body(std::false_type{});

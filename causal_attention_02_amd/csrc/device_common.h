@@ -152,6 +152,8 @@ struct ScoreCoef {
   float p1, p3, p5, p7, p9;  // polynomial modes: y = a * (p1 + a^2 (p3 + a^2 (p5 + ...)))
   float inv_k1_sq;   // 1 / (c log2e)^2 : tanh^2 = (y / (c log2e))^2
   float g2, g4;      // kScoreCapPoly5: sech^2 = 1 + a^2 (g2 + a^2 g4)
+  float mask_acc;    // raw score standing in for a masked entry (not kScoreCapExp): weight 0,
+                     // finite slope factor
 };
 
 // Returns y - shift (log2 units).  With T2 also *t2 = tanh^2(S_pre / c) (exp / degree-9

@@ -63,6 +63,36 @@ inline ScoreSetup make_score_setup(float scale, float softcap, int D, int qk_nor
     s.coef.g4 = (float)(2.0 / 3 * x * x * x * x);
   } else {
     s.mode = kScoreCapExp;
+  }
+  // The raw score that stands in for a masked entry of an edge tile, so that masked and
+  // unmasked tiles share one body (set before the score transform).  Without a bound on the
+  // shift (plain scores), -1e30.  The polynomial modes run under the QK-norm bound, so a row's
+  // shift lies within about +-60 (log2 units); their transform is a * q(a^2) with q >= 0.72 p1
+  // for every a (both truncations of tanh(x)/x stay above 0.72), so a = -1024 / (0.72 p1)
+  // gives y <= -1024: a weight of exactly 0 under any such shift, with the slope factor of the
+  // backward still finite.  Checked below with the kernels' own float formulas.
+  if (s.mode == kScoreScale) {
+    s.coef.mask_acc = -1.0e30f;
+  } else if (s.mode != kScoreCapExp) {
+    const float m = (float)(-1024.0 / (0.72 * (double)s.coef.p1));
+    const float a2 = m * m;
+    bool ok;
+    if (s.mode == kScoreCapPoly5) {
+      const float y = m * fmaf(a2, fmaf(a2, s.coef.p5, s.coef.p3), s.coef.p1);
+      const float g = fmaf(a2, fmaf(a2, s.coef.g4, s.coef.g2), 1.f);
+      ok = isfinite(y) && y <= -1024.f && isfinite(g);
+    } else {
+      float q = fmaf(a2, s.coef.p9, s.coef.p7);
+      q = fmaf(a2, q, s.coef.p5);
+      q = fmaf(a2, q, s.coef.p3);
+      q = fmaf(a2, q, s.coef.p1);
+      const float u = m * q;
+      ok = isfinite(u) && u <= -1024.f && isfinite(u * u * s.coef.inv_k1_sq);
+    }
+    if (ok) s.coef.mask_acc = m;
+    else s.mode = kScoreCapExp;  // the general form (masks after the transform)
+  }
+  if (s.mode == kScoreCapExp) {
     s.coef.k0 = (float)(2.0 * scale * log2e / softcap);
     s.coef.k1 = (float)(softcap * log2e);
     s.coef.inv_k1_sq = (float)(1.0 / ((double)s.coef.k1 * s.coef.k1));
