@@ -267,6 +267,7 @@ def main():
                 kk, vv = cps[i % len(cps)]
                 bd.attn_decode(tq, kk, vv, tl, opts_of(w), out=od, workspace=wsp)
 
+            settle(one)
             for i in range(args.warmup):
                 one(i)
             ms = timed(one, args.steps) / args.steps
