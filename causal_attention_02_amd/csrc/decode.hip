@@ -80,72 +80,10 @@ struct RunState {
   float m, l, o[NE];
 };
 
-// Merge two states: both are rescaled to the larger maximum (exact softmax identity).
-template <int NE>
-__device__ __forceinline__ void merge_state(RunState<NE>& s, float mp, float lp, const float* op) {
-  const float mn = fmaxf(s.m, mp);
-  const float fa = exp2_fast(s.m - mn), fb = exp2_fast(mp - mn);
-  s.l = s.l * fa + lp * fb;
-#pragma unroll
-  for (int e = 0; e < NE; ++e) s.o[e] = s.o[e] * fa + op[e] * fb;
-  s.m = mn;
-}
-
 // A DPP lane permutation of x (CTRL: the dpp_ctrl encoding).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Rotation by 4 or 8 lanes inside each row of 16 (DPP row_ror:4 / row_ror:8).
-template <int R>
-__device__ __forceinline__ float dpp_ror(float x) {
-  static_assert(R == 4 || R == 8, "row rotations by 4 or 8 lanes");
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), R == 4 ? 0x124 : 0x128,
-                                                    0xf, 0xf, false));
-}
-
-// All-reduce of the states over the 64 / LPR lanes that share (lane % LPR): DPP row rotations
-// by 4 (when LPR = 4) and 8 inside each row of 16 lanes, then swaps across rows (xor 16, 32).
-template <int NE, int LPR>
-__device__ __forceinline__ void merge_rows(RunState<NE>& s) {
-  if constexpr (LPR == 4) {
-    float op[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) op[e] = dpp_ror<4>(s.o[e]);
-    merge_state<NE>(s, dpp_ror<4>(s.m), dpp_ror<4>(s.l), op);
-  }
-  {
-    float op[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) op[e] = dpp_ror<8>(s.o[e]);
-    merge_state<NE>(s, dpp_ror<8>(s.m), dpp_ror<8>(s.l), op);
-  }
-  const int lane = threadIdx.x & 63;
-  {
-    // v_permlane16_swap(x, x): a lane in an even row of 16 gets (x[l], x[l + 16]), one in an
-    // odd row (x[l - 16], x[l]); the partner's value is the other half.
-    const bool odd = (lane >> 4) & 1;
-    auto sw = [odd](float x) {
-      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      return __uint_as_float(odd ? r[0] : r[1]);
-    };
-    float op[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) op[e] = sw(s.o[e]);
-    merge_state<NE>(s, sw(s.m), sw(s.l), op);
-  }
-  {
-    const bool hi = lane >= 32;
-    auto sw = [hi](float x) {
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      return __uint_as_float(hi ? r[0] : r[1]);
-    };
-    float op[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) op[e] = sw(s.o[e]);
-    merge_state<NE>(s, sw(s.m), sw(s.l), op);
-  }
 }
 
 // Lane map of one cache row: LPR lanes (4 or 8), lane j owning granules j, j + LPR, ... of GB
@@ -180,9 +118,15 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
   constexpr int kRowsPerStep = 64 / LPR;  // rows a wave covers per step
   constexpr int kRowsPerWave = kRowsPerStep * NSTEP;
   constexpr int kPass = NW * kRowsPerWave;  // rows per workgroup pass
+  constexpr int RL = 64 / LPR;  // row groups of lanes per wave
+  // Rescaled states of every row group for the merge: [wave][row group] rows of HPB x D, the
+  // row stride padded to 4 banks mod 64 so that the 16-byte writes of a wave's row groups
+  // fall on distinct banks.
+  constexpr int kRowStride = HPB * D + (4 - (HPB * D) % 64 + 64) % 64;
   __shared__ float sq[HPB][D];
-  __shared__ float sm[NW][HPB], sl[NW][HPB];
-  __shared__ float so[NW][HPB][D];
+  __shared__ float sm[NW][HPB];
+  __shared__ float sl[NW][RL][HPB];
+  __shared__ __attribute__((aligned(16))) float so[NW * RL * kRowStride];
 
   const int G = a.Hq / a.Hkv;
   const int nsub = G / HPB;
@@ -385,20 +329,46 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
     compute(b1, pass + 1);
   }
 
-  // Merge the lanes of each wave that own the same part of the rows, then the waves.
+  // Merge all row groups at once.  The lanes of a row group share its scores, so they hold the
+  // same (m, l) and split its output elements.  First the workgroup's largest reference per
+  // head (DPP and lane swaps inside each wave, then the waves through LDS); each lane rescales
+  // its own (l, o) to it; then every thread sums one output element over the row groups
+  // through LDS: no exp or maximum per merge step.
+  auto wave_max = [lane](float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));   // xor 1
+    x = fmaxf(x, dpp_f<0x4E>(x));   // xor 2
+    x = fmaxf(x, dpp_f<0x141>(x));  // mirror inside 8 lanes
+    x = fmaxf(x, dpp_f<0x140>(x));  // mirror inside 16 lanes
+    {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      x = fmaxf(x, __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]));
+    }
+    {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      x = fmaxf(x, __uint_as_float(lane >= 32 ? r[0] : r[1]));
+    }
+    return x;
+  };
 #pragma unroll
-  for (int hh = 0; hh < HPB; ++hh) merge_rows<NE, LPR>(st_[hh]);
-  if (lane < LPR) {
+  for (int hh = 0; hh < HPB; ++hh) {
+    const float wm = wave_max(st_[hh].m);
+    if (lane == 0) sm[w][hh] = wm;
+  }
+  __syncthreads();
+  {
+    float* row = so + (w * RL + rq) * kRowStride;
 #pragma unroll
     for (int hh = 0; hh < HPB; ++hh) {
-      if (lane == 0) {
-        sm[w][hh] = st_[hh].m;
-        sl[w][hh] = st_[hh].l;
-      }
+      float M = sm[0][hh];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm[ww][hh]);
+      // A row group that saw no active row holds m = kNegBig, l = 0, o = 0: factor 0.
+      const float f = exp2_fast(st_[hh].m - M);
+      if (j8 == 0) sl[w][rq][hh] = st_[hh].l * f;
 #pragma unroll
       for (int u = 0; u < NG; ++u)
 #pragma unroll
-        for (int e = 0; e < EPG; ++e) so[w][hh][RM::dim(j8, u, e)] = st_[hh].o[EPG * u + e];
+        for (int e = 0; e < EPG; ++e) row[hh * D + RM::dim(j8, u, e)] = st_[hh].o[EPG * u + e] * f;
     }
   }
   __syncthreads();
@@ -409,10 +379,9 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
     for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm[ww][hh]);
     float lt = 0.f, ot = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = exp2_fast(sm[ww][hh] - M);
-      lt += sl[ww][hh] * f;
-      ot += so[ww][hh][d] * f;
+    for (int g2 = 0; g2 < NW * RL; ++g2) {
+      lt += sl[g2 / RL][g2 % RL][hh];
+      ot += so[g2 * kRowStride + hh * D + d];
     }
     if (nact == 1) {
       // The only chunk of this sequence: write the normalised output directly.
