@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
   constexpr int kRowStride = HPB * D + (4 - (HPB * D) % 64 + 64) % 64;
   __shared__ float sq[HPB][D];
   __shared__ float sm[NW][HPB];
-  __shared__ float sl[NW][RL][HPB];
+  __shared__ float sl[NW][HPB];
   __shared__ __attribute__((aligned(16))) float so[NW * RL * kRowStride];
 
   const int G = a.Hq / a.Hkv;
@@ -334,24 +334,27 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
   // head (DPP and lane swaps inside each wave, then the waves through LDS); each lane rescales
   // its own (l, o) to it; then every thread sums one output element over the row groups
   // through LDS: no exp or maximum per merge step.
-  auto wave_max = [lane](float x) {
-    x = fmaxf(x, dpp_f<0xB1>(x));   // xor 1
-    x = fmaxf(x, dpp_f<0x4E>(x));   // xor 2
-    x = fmaxf(x, dpp_f<0x141>(x));  // mirror inside 8 lanes
-    x = fmaxf(x, dpp_f<0x140>(x));  // mirror inside 16 lanes
+  // All-lane reduction of a wave: DPP inside rows of 16 lanes, then lane swaps across rows.
+  auto wave_reduce = [lane](float x, auto op) {
+    x = op(x, dpp_f<0xB1>(x));   // xor 1
+    x = op(x, dpp_f<0x4E>(x));   // xor 2
+    x = op(x, dpp_f<0x141>(x));  // mirror inside 8 lanes
+    x = op(x, dpp_f<0x140>(x));  // mirror inside 16 lanes
     {
       auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      x = fmaxf(x, __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]));
+      x = op(x, __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]));
     }
     {
       auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      x = fmaxf(x, __uint_as_float(lane >= 32 ? r[0] : r[1]));
+      x = op(x, __uint_as_float(lane >= 32 ? r[0] : r[1]));
     }
     return x;
   };
+  auto fmax_op = [](float x, float y) { return fmaxf(x, y); };
+  auto add_op = [](float x, float y) { return x + y; };
 #pragma unroll
   for (int hh = 0; hh < HPB; ++hh) {
-    const float wm = wave_max(st_[hh].m);
+    const float wm = wave_reduce(st_[hh].m, fmax_op);
     if (lane == 0) sm[w][hh] = wm;
   }
   __syncthreads();
@@ -364,7 +367,9 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
       for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm[ww][hh]);
       // A row group that saw no active row holds m = kNegBig, l = 0, o = 0: factor 0.
       const float f = exp2_fast(st_[hh].m - M);
-      if (j8 == 0) sl[w][rq][hh] = st_[hh].l * f;
+      // The wave's rescaled weight sum (one lane per row group carries its l).
+      const float lw = wave_reduce(j8 == 0 ? st_[hh].l * f : 0.f, add_op);
+      if (lane == 0) sl[w][hh] = lw;
 #pragma unroll
       for (int u = 0; u < NG; ++u)
 #pragma unroll
@@ -379,10 +384,9 @@ __global__ __launch_bounds__(64 * kDecWaves, (dec_min_blocks<D, HPB, LPR>())) vo
     for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm[ww][hh]);
     float lt = 0.f, ot = 0.f;
 #pragma unroll
-    for (int g2 = 0; g2 < NW * RL; ++g2) {
-      lt += sl[g2 / RL][g2 % RL][hh];
-      ot += so[g2 * kRowStride + hh * D + d];
-    }
+    for (int ww = 0; ww < NW; ++ww) lt += sl[ww][hh];
+#pragma unroll
+    for (int g2 = 0; g2 < NW * RL; ++g2) ot += so[g2 * kRowStride + hh * D + d];
     if (nact == 1) {
       // The only chunk of this sequence: write the normalised output directly.
       a.o[((int64_t)b * a.Hq + h0 + hh) * D + d] = to_bf16(ot / lt);
