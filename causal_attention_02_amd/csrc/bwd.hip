@@ -882,9 +882,15 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
         }
       };
       // Gradient of element r of block qb: P (dV operand) into sacc, dS into pacc.
-      auto grad = [&](int qb, int r) {
+      // LSE log2(e) of half h of block qb (elements 8h .. 8h + 7: two runs of four rows), read
+      // as two 16-byte loads ahead of the gradients that use them.
+      auto lse_half = [&](int qb, int h, float4 (&lv)[2]) {
+        lv[0] = *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * h);
+        lv[1] = *reinterpret_cast<const float4*>(sl + qb * 32 + 4 * gl + 16 * h + 8);
+      };
+      auto grad = [&](int qb, int r, const float4 (&lv)[2]) {
         const int qo = 8 * (r >> 2) + (r & 3);
-        const float lse = sl[qb * 32 + 4 * gl + 8 * (r >> 2) + (r & 3)];
+        const float lse = pick(lv[(r >> 2) & 1], r & 3);
         float gf;
         float y = score_grad<MODE>(sacc[qb][r], a.sc, lse, &gf);
         if constexpr (decltype(masked)::value)
@@ -916,6 +922,8 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
       // dV / dK products of quarter (qb, t), step db carrying gradient elements
       // [g0 + 8 db / NDB, g0 + 8 (db + 1) / NDB) of block gq (none when gq < 0).
       auto quarter = [&](int qb, int t, int gq, int g0) {
+        float4 lv[2];
+        if (gq >= 0) lse_half(gq, g0 / 8, lv);
         bf16x8 ot = tr_read_pair(so + tr_off(qb, t, 0), so + tr_off(qb, t, 0) + 8 * LD);
         bf16x8 qt_ = tr_read_pair(sq + tr_off(qb, t, 0), sq + tr_off(qb, t, 0) + 8 * LD);
         __builtin_amdgcn_sched_barrier(0);
@@ -929,7 +937,7 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
           }
           if (gq >= 0) {
 #pragma unroll
-            for (int r = g0 + 8 * db / NDB; r < g0 + 8 * (db + 1) / NDB; ++r) grad(gq, r);
+            for (int r = g0 + 8 * db / NDB; r < g0 + 8 * (db + 1) / NDB; ++r) grad(gq, r, lv);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -944,14 +952,20 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
         pacc[0] = mfma32(oa, bv[s], pacc[0]);
       }
       __builtin_amdgcn_sched_barrier(0);
+      {
+        float4 lv[2];
+        lse_half(0, 0, lv);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) grad(0, r);
+        for (int r = 0; r < 8; ++r) grad(0, r, lv);
+      }
       pack(0, 0);
       quarter(0, 0, -1, 0);
       // Block 1's products beside block 0's second-half gradient.
       setup(1);
       bf16x8 qa = ld16<bf16x8>(sq + qk_off(1, 0));
       bf16x8 oa = ld16<bf16x8>(so + qk_off(1, 0));
+      float4 lv1[2];
+      lse_half(0, 1, lv1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -962,7 +976,7 @@ __global__ __launch_bounds__(256, (D >= 128 || (DROP && D >= 96)) ? 1 : 2) void 
           oa = ld16<bf16x8>(so + qk_off(1, s + 1));
         }
 #pragma unroll
-        for (int r = 8 + 8 * s / NS; r < 8 + 8 * (s + 1) / NS; ++r) grad(0, r);
+        for (int r = 8 + 8 * s / NS; r < 8 + 8 * (s + 1) / NS; ++r) grad(0, r, lv1);
         __builtin_amdgcn_sched_barrier(0);
       }
       pack(0, 1);
