@@ -542,14 +542,14 @@ def main():
         G = w.Hq // w.Hkv
         kw = okw(w)
 
-        def slice_c3(i):
+        def slice_181m(i):
             b, g = i % w.B, (i // w.B) % w.Hkv
             hs = slice(g * G, (g + 1) * G)
             attention_forward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], **kw)
             attention_backward(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
                                dO[b:b + 1, hs], **kw)
 
-        units, el = run_for(args.cpu_seconds, slice_c3)
+        units, el = run_for(args.cpu_seconds, slice_181m)
         slice_flops = train_flops(w.with_(B=1, Hq=G, Hkv=1))
         cpu = {"value": slice_flops * units / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
                "kind": "oracle",
@@ -561,7 +561,7 @@ def main():
                                 "the rest of the oracle is one Python thread"}}
         if threadpool_limits is not None:
             with threadpool_limits(limits=1):
-                n1, el1 = run_for(args.cpu_seconds / 3, slice_c3)
+                n1, el1 = run_for(args.cpu_seconds / 3, slice_181m)
             cpu["single_core"] = {"value": slice_flops * n1 / el1 / 1e12, "unit": "TFLOP/s",
                                   "cores": 1, "sample": f"{n1} slices in {el1:.1f} s"}
         log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s over {units} slices")
@@ -584,12 +584,12 @@ def main():
         n, el = run_for(3.0, fb2)
         per[w2.name] = {"ms_per_step": el / n * 1e3, "TFLOP/s": train_flops(w2) * n / el / 1e12,
                         "sample": f"{n} whole fwd+bwd steps in {el:.1f} s"}
-        w5 = WORKLOADS["gqa181m_decode"]
-        qd5, kc5, vc5, lens5 = make_decode_inputs(w5)
-        dkw = {x: y for x, y in okw(w5).items() if x != "window"}
-        n, el = run_for(3.0, lambda i: attention_decode(qd5, kc5, vc5, lens5, **dkw))
-        per[w5.name] = {"us_per_call": el / n * 1e6,
-                        "GB/s": decode_bytes(w5, lens5) * n / el / 1e9,
+        wdec = WORKLOADS["gqa181m_decode"]
+        qdd, kcd, vcd, lensd = make_decode_inputs(wdec)
+        dkw = {x: y for x, y in okw(wdec).items() if x != "window"}
+        n, el = run_for(3.0, lambda i: attention_decode(qdd, kcd, vcd, lensd, **dkw))
+        per[wdec.name] = {"us_per_call": el / n * 1e6,
+                        "GB/s": decode_bytes(wdec, lensd) * n / el / 1e9,
                         "sample": f"{n} whole decode calls (64 sequences) in {el:.1f} s"}
         cpu["per_config"] = per
         log(f"[bench] cpu oracle per config: {per}")
