@@ -340,6 +340,29 @@ def test_decode_tickets_return_to_zero():
         assert e <= TOL_O, (lens, e)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 64), (6, 2, 32), (12, 2, 64), (4, 4, 128)])
+def test_decode_group_sizes(Hq, Hkv, D):
+    """GQA groups of 4, 3 and 6 query heads (four, three and three heads per workgroup) and
+    plain MHA at d = 128, each with one chunk per cache (four lanes per row) and with chunked
+    caches (eight lanes per row, in-kernel merge); rows past the length are NaN."""
+    w = Workload("dec_groups", B=6, T=520, Hq=Hq, Hkv=Hkv, D=D, softcap=30.0, rope=True,
+                 decode=True, backward=False, seed=13)
+    _say(f"case decode groups Hq={Hq} Hkv={Hkv} D={D}")
+    q, kc, vc, _ = make_decode_inputs(w)
+    lens = np.array([520, 1, 200, 0, 333, 64], dtype=np.int32)
+    kc, vc = kc.copy(), vc.copy()
+    for b, L in enumerate(lens):
+        kc[b, :, L:] = np.nan
+        vc[b, :, L:] = np.nan
+    kw = {k: v for k, v in oracle_kw(w).items() if k != "window"}
+    ref = attention_decode(q, np.nan_to_num(kc), np.nan_to_num(vc), lens, **kw)
+    for sl in (0, 576, 128):
+        o = gpu_decode(w, q, kc, vc, lens, split_len=sl)
+        assert np.isfinite(o).all(), sl
+        e = rel_l2(o, ref)
+        assert e <= TOL_O, (sl, e)
+
+
 def test_decode_matches_last_forward_row():
     """Decode over a cache of rotated keys equals the last row of the training forward."""
     import torch
