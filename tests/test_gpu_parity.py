@@ -340,11 +340,12 @@ def test_decode_tickets_return_to_zero():
         assert e <= TOL_O, (lens, e)
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 64), (6, 2, 32), (12, 2, 64), (4, 4, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 64), (6, 2, 32), (12, 2, 64), (4, 4, 128), (4, 2, 128)])
 def test_decode_group_sizes(Hq, Hkv, D):
-    """GQA groups of 4, 3 and 6 query heads (four, three and three heads per workgroup) and
-    plain MHA at d = 128, each with one chunk per cache (four lanes per row) and with chunked
-    caches (eight lanes per row, in-kernel merge); rows past the length are NaN."""
+    """GQA groups of 4, 3 and 6 query heads (four, three and three heads per workgroup), plain
+    MHA at d = 128 and pairs of heads at d = 128 (the largest merge buffer), each with one chunk
+    per cache (four lanes per row) and with chunked caches (eight lanes per row, in-kernel
+    merge); rows past the length are NaN."""
     w = Workload("dec_groups", B=6, T=520, Hq=Hq, Hkv=Hkv, D=D, softcap=30.0, rope=True,
                  decode=True, backward=False, seed=13)
     _say(f"case decode groups Hq={Hq} Hkv={Hkv} D={D}")
